@@ -1,0 +1,244 @@
+"""Benchmark of the causal GQA prefill hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one attn_causal_prefill call (main kernel and, when the key range
+is split, the combine kernel) over inputs already resident in HBM.  The
+default workload is the long-context D=128 chunk: B=1, Hq=16, Hkv=2,
+Lq=1024, Lkv=131072, end-aligned causal.  Throughput counts only unmasked
+(query, key) pairs, 4*D FLOP each.  Prints ONE JSON line.
+
+The roofline object prices the step against the bf16 dense MFMA peak, with
+the step time measured by HIP events on the stream the kernels run on.  The
+cpu_baseline object times the fp64 oracle on a bounded row sample of the same
+workload on the host cores.  Varlen workloads (--workload varlen_pinned,
+varlen_short) report HBM GB/s of algorithmic bytes instead.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA prefill TFLOP/s (unmasked pairs) + % bf16 MFMA peak, Lkv=131072"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (AMD: 2.5 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0
+SRC = os.path.join(ROOT, "causal_gqa_prefill_flash_amd", "csrc", "attn.hip")
+
+
+def prefill_pairs(B, Hq, Lq, Lkv, q_pos0, window):
+    """Unmasked (query, key) pairs: row i at position q_pos0+i sees keys
+    max(0, p-W+1) .. min(Lkv-1, p)."""
+    p = torch.arange(Lq, dtype=torch.int64) + q_pos0
+    hi = torch.clamp(p, max=Lkv - 1)
+    lo = torch.clamp(p - window + 1, min=0) if window > 0 else torch.zeros_like(p)
+    n = torch.clamp(hi - lo + 1, min=0)
+    return int(n.sum()) * B * Hq
+
+
+def varlen_pairs_and_bytes(info, attr, Hq, Hkv, D):
+    """Unmasked pairs, and algorithmic HBM bytes (visible K/V rows once per
+    KV head, Q read and O written once per covered row, uncovered rows
+    written once) of a varlen step."""
+    pairs = 0
+    kv_rows = 0
+    for s in range(info.shape[0]):
+        q_start, q_len, col, kv_end = (int(x) for x in info[s])
+        causal, W, _ = (int(x) for x in attr[s])
+        lo_all, hi_all = None, 0
+        for j in range(q_len):
+            p = kv_end - q_len + j
+            hi = min(kv_end - 1, p) if causal else kv_end - 1
+            lo = max(0, p - W + 1) if W > 0 else 0
+            pairs += max(0, hi - lo + 1)
+            if hi >= lo:
+                lo_all = lo if lo_all is None else min(lo_all, lo)
+                hi_all = max(hi_all, hi + 1)
+        if lo_all is not None:
+            kv_rows += hi_all - lo_all
+    return pairs * Hq, kv_rows
+
+
+def src_digest():
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, when they
+    were taken on the kernel source that is built now; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("src_sha256_16") != src_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def cpu_baseline_prefill(q, k, v, w, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of query rows."""
+    import oracle
+    B, Hq, Lq, D = q.shape
+    Lkv = k.shape[2]
+    q_pos0 = w["q_pos0"] if w["q_pos0"] is not None else Lkv - Lq
+    n = 2
+    while True:
+        rows = sorted(set(int(x) for x in torch.linspace(0, Lq - 1, n).round().tolist()))
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, 1.0 / math.sqrt(D), q_pos0=q_pos0, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or n >= Lq:
+            break
+        n = min(Lq, max(n * 2, int(n * budget_s / 4 / max(dt, 1e-3))))
+    p = torch.tensor(rows, dtype=torch.int64) + q_pos0
+    vis = torch.clamp(torch.clamp(p, max=Lkv - 1) + 1, min=0)
+    pairs = int(vis.sum()) * B * Hq
+    return {"value": 4.0 * D * pairs / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d query rows (evenly spaced), all %d heads, fp64, %.1f s"
+                      % (len(rows), Lq, Hq, dt)}
+
+
+def bench_prefill(args, name):
+    import causal_gqa_prefill_flash_amd as attn
+    from causal_gqa_prefill_flash_amd import synth
+    w = synth.PREFILL_WORKLOADS[name]
+    B, Hq, Hkv, D, Lq, Lkv = w["B"], w["Hq"], w["Hkv"], w["D"], w["Lq"], w["Lkv"]
+    q_pos0 = w["q_pos0"] if w["q_pos0"] is not None else Lkv - Lq
+    qc, kc, vc = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=w["wid"])
+    dev = torch.device("cuda:0")
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = attn.prefill_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        attn.causal_prefill(q, k, v, out=out, q_pos0=q_pos0, workspace=ws)
+
+    ms = time_calls(step, args.steps, args.warmup)
+    pairs = prefill_pairs(B, Hq, Lq, Lkv, q_pos0, 0)
+    flops = 4.0 * D * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal GQA prefill %s" % name, "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "D": D, "Lq": Lq, "Lkv": Lkv, "q_pos0": q_pos0,
+                   "unmasked_pairs": pairs},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(name),
+                     "algorithmic_flop_per_launch": flops,
+                     "timed": "whole call (main + split-combine kernels), HIP events on the "
+                              "launch stream"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(qc, kc, vc, w)
+    return line
+
+
+def bench_varlen(args, name):
+    import causal_gqa_prefill_flash_amd as attn
+    from causal_gqa_prefill_flash_amd import synth
+    st = synth.VARLEN_STORE
+    rows, cols, Hkv, D, Hq = st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"]
+    if name == "varlen_pinned":
+        info, attr, T = synth.pinned_varlen_table()
+    else:  # short-query step: every segment decode-like over a full flat column
+        qlens = [1, 4, 16, 1, 4, 16, 4, 1]
+        rows_info, t = [], 0
+        for s, ql in enumerate(qlens):
+            rows_info.append((t, ql, s, rows))
+            t += ql
+        info = torch.tensor(rows_info, dtype=torch.int32)
+        attr = torch.tensor([(1, 0, 0)] * len(qlens), dtype=torch.int32)
+        T = t
+    dev = torch.device("cuda:0")
+    # rotate over several store copies so the 256 MB last-level cache cannot hold them
+    ncopy = 8
+    q = synth.varlen_inputs(T, 8, cols, Hkv, D, Hq, wid=60)[0].to(dev)
+    stores = []
+    for c in range(ncopy):
+        ks = synth.randn_bf16((rows, cols, Hkv, D), 7000 + c).to(dev)
+        vs = synth.randn_bf16((rows, cols, Hkv, D), 7100 + c).to(dev)
+        stores.append((ks, vs))
+    si, sa = info.to(dev), attr.to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(attn.varlen_workspace_bytes(len(info), T, Hq, Hkv, D, rows, cols),
+                     dtype=torch.uint8, device=dev)
+    it = [0]
+
+    def step():
+        ks, vs = stores[it[0] % ncopy]
+        it[0] += 1
+        attn.sdpa_varlen(q, ks, vs, si, seg_attr=sa, out=out, workspace=ws)
+
+    ms = time_calls(step, args.steps, args.warmup)
+    pairs, kv_rows = varlen_pairs_and_bytes(info, attr, Hq, Hkv, D)
+    nbytes = kv_rows * Hkv * D * 2 * 2 + T * Hq * D * 2 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "varlen SDPA HBM GB/s (algorithmic bytes)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "rows": rows, "cols": cols, "Hkv": Hkv, "D": D, "Hq": Hq,
+                   "T": T, "S": int(info.shape[0]), "unmasked_pairs": pairs,
+                   "store_copies_rotated": ncopy},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profile(name), "algorithmic_bytes_per_launch": nbytes,
+                     "tflops_unmasked": round(4.0 * D * pairs / (ms * 1e-3) / 1e12, 3)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d128_lq1k_lkv128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload.startswith("varlen"):
+        line = bench_varlen(args, args.workload)
+    else:
+        line = bench_prefill(args, args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

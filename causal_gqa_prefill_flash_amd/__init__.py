@@ -1,1 +1,194 @@
-"""Causal GQA prefill and varlen SDPA for MI355X (gfx950)."""
+"""Causal GQA prefill and varlen SDPA on MI355X (gfx950): the Python binding.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn.so`` (built from ``csrc/attn.hip`` by ``build.py``),
+called through its C ABI (``include/attn.h``).  PyTorch provides device
+memory and the current stream.  There is no fallback: if the library is
+missing or the tensors are not on a ROCm device, calls raise.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP = 1, 2, 4, 8, 16
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("attn status %d: %s" % (status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libattn.so is not built: run causal_gqa_prefill_flash_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    I64A = ctypes.POINTER(ctypes.c_int64)
+    L.attn_abi_version.restype = I
+    L.attn_abi_version.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_causal_prefill_workspace.restype = SZ
+    L.attn_causal_prefill_workspace.argtypes = [I, I, I, I, I, I]
+    L.attn_causal_prefill.restype = I
+    L.attn_causal_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float,
+                                      I64A, I64A, I64A, I64A, I64, I, P, SZ, P]
+    L.attn_sdpa_varlen_workspace.restype = SZ
+    L.attn_sdpa_varlen_workspace.argtypes = [I, I, I, I, I, I, I]
+    L.attn_sdpa_varlen.restype = I
+    L.attn_sdpa_varlen.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, ctypes.c_float,
+                                   I, I, I, I64A, I64A, I64A, I64A, P, SZ, P]
+    L.attn_varlen_read_error.restype = I
+    L.attn_varlen_read_error.argtypes = [P, I, I, P, ctypes.POINTER(ctypes.c_int32)]
+    _lib = L
+    return L
+
+
+def last_error():
+    return lib().attn_last_error().decode()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, last_error())
+
+
+def _strides(t, n):
+    s = t.stride()
+    if len(s) != n:
+        raise ValueError("expected a %d-d tensor, got shape %s" % (n, tuple(t.shape)))
+    return (ctypes.c_int64 * n)(*s)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _gpu(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a ROCm device tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise ValueError("%s must be bfloat16" % name)
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace of %d bytes is too small (%d needed)" %
+                             (workspace.numel() * workspace.element_size(), nbytes))
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D):
+    return lib().attn_causal_prefill_workspace(B, Hq, Hkv, Lq, Lkv, D)
+
+
+def causal_prefill(q, k, v, out=None, scale=None, q_pos0=None, window=0, workspace=None):
+    """Causal GQA prefill: out[b,h,i] = softmax attention of query row i
+    (position q_pos0 + i, default Lkv - Lq) over keys j <= that position
+    (and > position - window when window > 0), key/value head h // (Hq/Hkv).
+
+    q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D] bf16 on the device, any strides with a
+    unit innermost stride.  Returns ``out`` ([B,Hq,Lq,D] bf16).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _gpu(t, n)
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not agree: %s %s %s" % (q.shape, k.shape, v.shape))
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _gpu(out, "out")
+        if tuple(out.shape) != (B, Hq, Lq, D):
+            raise ValueError("out has shape %s" % (tuple(out.shape),))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_pos0 is None:
+        q_pos0 = Lkv - Lq
+    with torch.cuda.device(q.device):
+        need = prefill_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
+        ws = _workspace(need, q.device, workspace)
+        st = lib().attn_causal_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lkv, D, float(scale),
+            _strides(q, 4), _strides(k, 4), _strides(v, 4), _strides(out, 4),
+            int(q_pos0), int(window), _ptr(ws), need, _stream())
+    _check(st)
+    return out
+
+
+def varlen_workspace_bytes(S, T, Hq, Hkv, D, rows, cols):
+    return lib().attn_sdpa_varlen_workspace(S, T, Hq, Hkv, D, rows, cols)
+
+
+def sdpa_varlen(q, k_store, v_store, seq_info, seg_attr=None, out=None, scale=None, causal=1,
+                window=0, ring_rows=0, workspace=None):
+    """Varlen SDPA over a [rows, cols, Hkv, D] column store driven by the
+    device table seq_info int32 [S,4] = (q_start, q_len, col, kv_end) and the
+    optional per-segment seg_attr int32 [S,3] = (causal, window, ring_rows).
+
+    q [T,Hq,D] packed rows; returns ``out`` [T,Hq,D] with every row written
+    (rows of no valid segment are zeros).  Pass ``workspace`` (uint8, at
+    least ``varlen_workspace_bytes``) to keep the call allocation-free, e.g.
+    under graph capture; read its error word with ``varlen_read_error``.
+    """
+    for t, n in ((q, "q"), (k_store, "k_store"), (v_store, "v_store")):
+        _gpu(t, n)
+    T, Hq, D = q.shape
+    rows, cols, Hkv, Dk = k_store.shape
+    if Dk != D or tuple(v_store.shape) != tuple(k_store.shape):
+        raise ValueError("store shapes do not agree")
+    if seq_info.dtype != torch.int32 or not seq_info.is_cuda or not seq_info.is_contiguous():
+        raise ValueError("seq_info must be a contiguous int32 device tensor")
+    S = seq_info.shape[0] if seq_info.numel() else 0
+    if seq_info.numel() and tuple(seq_info.shape) != (S, 4):
+        raise ValueError("seq_info must be [S, 4]")
+    if seg_attr is not None:
+        if (seg_attr.dtype != torch.int32 or not seg_attr.is_cuda or
+                not seg_attr.is_contiguous() or tuple(seg_attr.shape) != (S, 3)):
+            raise ValueError("seg_attr must be a contiguous int32 device tensor [S, 3]")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _gpu(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        need = varlen_workspace_bytes(S, T, Hq, Hkv, D, rows, cols)
+        ws = _workspace(need, q.device, workspace)
+        st = lib().attn_sdpa_varlen(
+            _ptr(q), _ptr(k_store), _ptr(v_store), _ptr(out), _ptr(seq_info), S,
+            _ptr(seg_attr), T, Hq, Hkv, D, rows, cols, float(scale), int(causal), int(window),
+            int(ring_rows), _strides(q, 3), _strides(k_store, 4), _strides(v_store, 4),
+            _strides(out, 3), _ptr(ws), need, _stream())
+    _check(st)
+    return out, ws
+
+
+def varlen_read_error(workspace, S, T):
+    """OR of the ATTN_SEG_* flags of the last varlen call on ``workspace``."""
+    e = ctypes.c_int32(0)
+    _check(lib().attn_varlen_read_error(_ptr(workspace), S, T, _stream(), ctypes.byref(e)))
+    return e.value

@@ -1,0 +1,982 @@
+// attn.hip -- causal GQA prefill and varlen SDPA for MI355X (gfx950, CDNA4).
+//
+// Flash-style attention: one pass over the keys with an online softmax
+// (exact running maximum, fp32 running sum, fp32 accumulator), bf16 MFMA for
+// both contractions, K/V tiles staged through LDS and shared by every query
+// head of a GQA group.  The operation is defined in
+// "[CUDA] Use Triton TMA for long-context causal prefill" (Summary) and
+// "[executorch][cuda] Add a length-aware Triton SDPA over per-sequence KV
+// columns" (description); the C ABI is declared in include/attn.h.
+//
+// Work decomposition (one workgroup = 4 waves = 128 query rows):
+//   rows of a workgroup = (query heads of one KV head) x (query positions);
+//   each wave owns 32 rows and keeps Q, the output accumulator, the running
+//   maximum and the running sum in registers for the whole key range.
+//   Keys stream in tiles of 64: K as [key][d] and V transposed as [d][key]
+//   in LDS; the next tile's global loads are in flight while the current
+//   tile is computed.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16): the score tile is computed
+// transposed, S^T = K Q^T (keys x rows), so each lane holds 16 scores of ONE
+// query row: row maxima and sums are in-lane plus a single exchange between
+// lanes l and l+32.  The same registers, rounded to bf16, are directly the
+// B operand of O^T = V^T P^T; V^T is stored in LDS with the key order inside
+// each 16-key group permuted (bits 2 and 3 of the key index swapped) to
+// match which keys each lane holds.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "attn.h"
+
+namespace {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kBM = kWaves * 32;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kPad = 8;           // LDS row padding (elements): 16 bytes
+constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
+constexpr int kMaxSplits = 16;
+constexpr int kFinishRows = 4;    // packed rows per workgroup of the varlen finish pass
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Rows of a workgroup: Gc query heads (of one GQA group) x P positions.
+struct RowMap {
+    int Gc, P, hchunks;
+};
+
+__host__ __device__ inline RowMap row_map(int g) {
+    RowMap r;
+    r.Gc = g < kBM ? g : kBM;
+    r.P = kBM / r.Gc;
+    r.hchunks = (g + r.Gc - 1) / r.Gc;
+    return r;
+}
+
+__host__ __device__ inline int varlen_qsplit(int P) { return P < kQSplitMax ? P : kQSplitMax; }
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ inline uint4 ld16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ inline bf16x8 lds_frag(const u16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Key/value rows of a flat [.., L, D] tensor.
+struct KVFlat {
+    const u16* kb;
+    const u16* vb;
+    int64_t ks, vs;
+    __device__ const u16* krow(int j) const { return kb + (int64_t)j * ks; }
+    __device__ const u16* vrow(int j) const { return vb + (int64_t)j * vs; }
+};
+
+// Key/value rows of one column of a [rows, cols, H, D] store; position k
+// lives at row k mod R.
+struct KVRing {
+    const u16* kb;
+    const u16* vb;
+    int64_t ks, vs;
+    int R;
+    __device__ const u16* krow(int j) const { return kb + (int64_t)(j % R) * ks; }
+    __device__ const u16* vrow(int j) const { return vb + (int64_t)(j % R) * vs; }
+};
+
+template <int D>
+struct TileRegs {
+    static constexpr int kChunks = kBN * D / 8;  // 16-byte chunks of one K tile
+    static constexpr int kPer = kChunks / kThreads;
+    static constexpr int kVItems = (kBN / 4) * (D / 8);  // (4-key quad, 8-d chunk)
+    uint4 k[kPer];
+    uint4 v[4];
+};
+
+// Global -> registers: the K/V rows of keys [k0, k0+kBN); keys >= k_hi read as 0.
+template <int D, class KV>
+__device__ inline void load_tile(TileRegs<D>& t, const KV& kv, int k0, int k_hi, int tid) {
+#pragma unroll
+    for (int it = 0; it < TileRegs<D>::kPer; ++it) {
+        int c = tid + it * kThreads;
+        int key = c / (D / 8), d8 = c % (D / 8);
+        int j = k0 + key;
+        t.k[it] = j < k_hi ? ld16(kv.krow(j) + 8 * d8) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < TileRegs<D>::kVItems) {
+        int quad = tid % (kBN / 4), d8 = tid / (kBN / 4);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            int j = k0 + 4 * quad + jj;
+            t.v[jj] = j < k_hi ? ld16(kv.vrow(j) + 8 * d8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+__device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// Registers -> LDS: K as Ks[key][d]; V transposed as Vt[d][perm(key)].
+template <int D>
+__device__ inline void store_tile(const TileRegs<D>& t, u16* Ks, u16* Vt, int tid) {
+    constexpr int KSTR = D + kPad, VSTR = kBN + kPad;
+#pragma unroll
+    for (int it = 0; it < TileRegs<D>::kPer; ++it) {
+        int c = tid + it * kThreads;
+        int key = c / (D / 8), d8 = c % (D / 8);
+        *reinterpret_cast<uint4*>(Ks + key * KSTR + 8 * d8) = t.k[it];
+    }
+    if (tid < TileRegs<D>::kVItems) {
+        int quad = tid % (kBN / 4), d8 = tid / (kBN / 4);
+        // keys 4*quad .. 4*quad+3 land at pos .. pos+3 within the permuted order
+        int pos = 16 * (quad >> 2) + 8 * (quad & 1) + 4 * ((quad >> 1) & 1);
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(&t.v[0]);
+        const uint32_t* b = reinterpret_cast<const uint32_t*>(&t.v[1]);
+        const uint32_t* c2 = reinterpret_cast<const uint32_t*>(&t.v[2]);
+        const uint32_t* d2 = reinterpret_cast<const uint32_t*>(&t.v[3]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint2 even = make_uint2(lo_pair(a[m], b[m]), lo_pair(c2[m], d2[m]));
+            uint2 odd = make_uint2(hi_pair(a[m], b[m]), hi_pair(c2[m], d2[m]));
+            *reinterpret_cast<uint2*>(Vt + (8 * d8 + 2 * m) * VSTR + pos) = even;
+            *reinterpret_cast<uint2*>(Vt + (8 * d8 + 2 * m + 1) * VSTR + pos) = odd;
+        }
+    }
+}
+
+// Per-lane online-softmax state of one query row (lanes l and l+32 share a row).
+template <int D>
+struct RowState {
+    f32x16 o[D / 32];  // O^T accumulator: d = 32*dt + 8*(r/4) + 4*(lane/32) + r%4
+    float m;           // running maximum of raw scores (-inf: nothing seen)
+    float l;           // this lane's share of the running sum
+};
+
+// Attend the keys [k_lo, k_hi) for the 32 rows of this wave.
+//   p_lane: position of this lane's row; p_min/p_max: extreme positions of
+//   the workgroup's rows (for the per-tile mask decision).
+template <int D, class KV>
+__device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
+                             int64_t p_lane, int64_t p_min, int64_t p_max, const bf16x8* qf,
+                             float c, RowState<D>& st, u16* Ks, u16* Vt) {
+    constexpr int KSTR = D + kPad, VSTR = kBN + kPad;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int lr = lane & 31, hh = lane >> 5;
+    if (k_lo >= k_hi) return;
+
+    TileRegs<D> regs;
+    load_tile<D>(regs, kv, k_lo, k_hi, tid);
+    for (int k0 = k_lo; k0 < k_hi; k0 += kBN) {
+        __syncthreads();  // every wave is done reading the previous tile
+        store_tile<D>(regs, Ks, Vt, tid);
+        __syncthreads();
+        if (k0 + kBN < k_hi) load_tile<D>(regs, kv, k0 + kBN, k_hi, tid);
+
+        // S^T = K Q^T: 32 keys x 32 rows per MFMA output
+        f32x16 s[kBN / 32];
+#pragma unroll
+        for (int t = 0; t < kBN / 32; ++t) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    lds_frag(Ks + (32 * t + lr) * KSTR + 16 * kk + 8 * hh), qf[kk], acc, 0, 0, 0);
+            s[t] = acc;
+        }
+
+        const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
+                               (window > 0 && (int64_t)k0 <= p_max - window);
+        if (need_mask) {
+#pragma unroll
+            for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    bool vis = key < k_hi && (!causal || key <= p_lane) &&
+                               (window <= 0 || key > p_lane - window);
+                    s[t][r] = vis ? s[t][r] : -INFINITY;
+                }
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(st.m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
+        const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m_use) * c);
+        st.m = m_new;
+        const float mc = m_use * c;
+
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
+                if (need_mask) p = s[t][r] == -INFINITY ? 0.f : p;
+                s[t][r] = p;
+                lsum += p;
+            }
+        st.l = st.l * alpha + lsum;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
+        }
+
+        // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+        for (int c4 = 0; c4 < kBN / 16; ++c4) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[c4 >> 1][8 * (c4 & 1) + e];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    lds_frag(Vt + (32 * dt + lr) * VSTR + 16 * c4 + 8 * hh), pb, st.o[dt], 0, 0,
+                    0);
+        }
+    }
+}
+
+// Q fragments of this lane's row (zeros for rows that do not exist);
+// the sign of a negative scale is folded into Q, which is exact.
+template <int D>
+__device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, bool negate) {
+    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
+    const uint32_t flip = negate ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        uint4 u = valid ? ld16(qrow + 16 * kk + 8 * hh) : make_uint4(0, 0, 0, 0);
+        u.x ^= flip;
+        u.y ^= flip;
+        u.z ^= flip;
+        u.w ^= flip;
+        qf[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(u16, x) | ((uint32_t)__builtin_bit_cast(u16, y) << 16);
+}
+
+// Final normalisation and bf16 store of this lane's row: o / l, 0 when l == 0.
+template <int D>
+__device__ inline void store_out(const RowState<D>& st, u16* orow, bool valid) {
+    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
+    float l = st.l + __shfl_xor(st.l, 32);
+    float inv = l > 0.f ? 1.f / l : 0.f;
+    if (!valid) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            int d = 32 * dt + 8 * a + 4 * hh;
+            uint2 w = make_uint2(pack_bf16x2(st.o[dt][4 * a] * inv, st.o[dt][4 * a + 1] * inv),
+                                 pack_bf16x2(st.o[dt][4 * a + 2] * inv, st.o[dt][4 * a + 3] * inv));
+            *reinterpret_cast<uint2*>(orow + d) = w;
+        }
+}
+
+// Split partial of this lane's row: unnormalised accumulator, log2-domain
+// maximum (m*c, -inf when nothing was visible) and the sum.
+template <int D>
+__device__ inline void store_partial(const RowState<D>& st, float c, float* po, float* pml,
+                                     bool valid) {
+    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
+    float l = st.l + __shfl_xor(st.l, 32);
+    if (!valid) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            int d = 32 * dt + 8 * a + 4 * hh;
+            *reinterpret_cast<float4*>(po + d) =
+                make_float4(st.o[dt][4 * a], st.o[dt][4 * a + 1], st.o[dt][4 * a + 2],
+                            st.o[dt][4 * a + 3]);
+        }
+    if (hh == 0) {
+        pml[0] = st.m == -INFINITY ? -INFINITY : st.m * c;
+        pml[1] = l;
+    }
+}
+
+template <int D>
+__device__ inline void init_state(RowState<D>& st) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
+    st.m = -INFINITY;
+    st.l = 0.f;
+}
+
+// Key range [lo, hi) of split `split` out of `nsplit` over [lo_all, hi_all).
+__device__ inline void split_range(int lo_all, int hi_all, int split, int nsplit, int* lo, int* hi) {
+    int span = hi_all - lo_all;
+    int chunk = (span + nsplit - 1) / nsplit;
+    chunk = (chunk + kBN - 1) / kBN * kBN;
+    int a = lo_all + split * chunk;
+    int b = a + chunk;
+    *lo = a < hi_all ? a : hi_all;
+    *hi = b < hi_all ? b : hi_all;
+}
+
+// ---------------------------------------------------------------- prefill
+
+struct PrefillArgs {
+    const u16* q;
+    const u16* k;
+    const u16* v;
+    u16* out;
+    float* part_o;   // [nsplit][B][Hq][Lq][D]
+    float* part_ml;  // [nsplit][B][Hq][Lq][2]
+    int B, Hq, Hkv, Lq, Lkv, window, nsplit;
+    float c;  // |scale| * log2(e)
+    int negate;
+    int64_t q_pos0;
+    int64_t qs[4], ks[4], vs[4], os[4];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) u16 Ks[kBN * (D + kPad)];
+    __shared__ __attribute__((aligned(16))) u16 Vt[D * (kBN + kPad)];
+
+    const int g = a.Hq / a.Hkv;
+    const RowMap rm = row_map(g);
+    const int qb = blockIdx.x / rm.hchunks, hc = blockIdx.x % rm.hchunks;
+    const int b = blockIdx.y / a.Hkv, hk = blockIdx.y % a.Hkv;
+    const int split = blockIdx.z;
+    const int q0 = qb * rm.P;
+    const int heads_here = min(rm.Gc, g - hc * rm.Gc);
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r = wave * 32 + (lane & 31);
+    const int hl = r / rm.P, pos = r % rm.P;
+    const int i = q0 + pos;
+    const bool valid = hl < heads_here && i < a.Lq;
+    const int h = hk * g + hc * rm.Gc + hl;
+
+    const int64_t p_min = a.q_pos0 + q0;
+    const int64_t p_max = a.q_pos0 + min(q0 + rm.P, a.Lq) - 1;
+    const int64_t p_lane = valid ? a.q_pos0 + i : p_max;
+
+    // visible keys of the whole workgroup, then this split's share
+    int64_t lo64 = a.window > 0 ? p_min - a.window + 1 : 0;
+    int64_t hi64 = p_max + 1 < a.Lkv ? p_max + 1 : a.Lkv;
+    if (lo64 < 0) lo64 = 0;
+    if (hi64 < lo64) hi64 = lo64;
+    int k_lo, k_hi;
+    split_range((int)lo64, (int)hi64, split, a.nsplit, &k_lo, &k_hi);
+
+    bf16x8 qf[D / 16];
+    load_q<D>(qf, a.q + b * a.qs[0] + (int64_t)h * a.qs[1] + (int64_t)i * a.qs[2], valid,
+              a.negate);
+
+    RowState<D> st;
+    init_state<D>(st);
+    KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
+              a.vs[2]};
+    attend_range<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, Ks, Vt);
+
+    if (a.nsplit == 1) {
+        store_out<D>(st, a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2], valid);
+    } else {
+        int64_t row = (((int64_t)split * a.B + b) * a.Hq + h) * a.Lq + i;
+        store_partial<D>(st, a.c, a.part_o + row * D, a.part_ml + row * 2, valid);
+    }
+}
+
+// Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
+// o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).
+template <int D>
+__device__ inline void combine_row(const float* po, const float* pml, int64_t split_stride_o,
+                                   int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[s * split_stride_ml]);
+    float L = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int s = 0; s < nsplit; ++s) {
+            float ms = pml[s * split_stride_ml];
+            if (ms == -INFINITY) continue;
+            float w = __builtin_amdgcn_exp2f(ms - M);
+            L += w * pml[s * split_stride_ml + 1];
+            float4 x = *reinterpret_cast<const float4*>(po + s * split_stride_o + d0);
+            acc[0] += w * x.x;
+            acc[1] += w * x.y;
+            acc[2] += w * x.z;
+            acc[3] += w * x.w;
+        }
+    }
+    float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                         pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    *reinterpret_cast<uint2*>(orow + d0) = o;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+    constexpr int TPR = D / 4;  // threads per row, 4 dims each
+    int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+    int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    if (row >= rows) return;
+    int d0 = (threadIdx.x % TPR) * 4;
+    int i = (int)(row % a.Lq);
+    int h = (int)((row / a.Lq) % a.Hq);
+    int b = (int)(row / ((int64_t)a.Lq * a.Hq));
+    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit, d0,
+                   a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]);
+}
+
+// ---------------------------------------------------------------- varlen
+
+struct VarlenArgs {
+    const u16* q;
+    const u16* k;
+    const u16* v;
+    u16* out;
+    const int32_t* seq_info;
+    const int32_t* seg_attr;
+    int32_t* err;    // one word per finish workgroup
+    float* part_o;   // [S][qsplit][Hq][nsplit][D]
+    float* part_ml;  // [S][qsplit][Hq][nsplit][2]
+    int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows, nsplit;
+    float c;
+    int negate;
+    int64_t qs[3], ks[4], vs[4], os[3];
+};
+
+struct Segment {
+    int q_start, q_len, col, kv_end;
+    int causal, window, R;
+    int flags;
+};
+
+// Decode and check segment s (the same rules as ATTN_SEG_* in attn.h).
+__device__ inline Segment read_segment(const VarlenArgs& a, int s) {
+    Segment g;
+    g.q_start = a.seq_info[4 * s + 0];
+    g.q_len = a.seq_info[4 * s + 1];
+    g.col = a.seq_info[4 * s + 2];
+    g.kv_end = a.seq_info[4 * s + 3];
+    int ring_rows;
+    if (a.seg_attr) {
+        g.causal = a.seg_attr[3 * s + 0];
+        g.window = a.seg_attr[3 * s + 1];
+        ring_rows = a.seg_attr[3 * s + 2];
+    } else {
+        g.causal = a.causal;
+        g.window = a.window;
+        ring_rows = a.ring_rows;
+    }
+    int f = 0;
+    if (g.q_start < 0 || g.q_len < 0 || (int64_t)g.q_start + g.q_len > a.T) f |= ATTN_SEG_QRANGE;
+    if (g.col < 0 || g.col >= a.cols - 1) f |= ATTN_SEG_COL;
+    if (ring_rows > a.rows) f |= ATTN_SEG_ATTR;
+    bool ring = ring_rows > 0;
+    g.R = ring ? ring_rows : a.rows;
+    if (g.kv_end < 0 || (!ring && g.kv_end > a.rows)) f |= ATTN_SEG_KVEND;
+    g.flags = f;
+    return g;
+}
+
+__device__ inline bool seg_splits(const Segment& g, int qsplit, int nsplit) {
+    return nsplit > 1 && g.q_len <= qsplit;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
+    __shared__ __attribute__((aligned(16))) u16 Ks[kBN * (D + kPad)];
+    __shared__ __attribute__((aligned(16))) u16 Vt[D * (kBN + kPad)];
+
+    const int g = a.Hq / a.Hkv;
+    const RowMap rm = row_map(g);
+    const int qsplit = varlen_qsplit(rm.P);
+    const int hk = blockIdx.y / rm.hchunks, hc = blockIdx.y % rm.hchunks;
+    const int split = blockIdx.z;
+
+    // the (segment, q-block) of this workgroup: blocks are numbered through
+    // the valid segments in table order
+    int blk = blockIdx.x, seg = -1, qb = 0;
+    Segment sg;
+    for (int s = 0; s < a.S; ++s) {
+        Segment x = read_segment(a, s);
+        if (x.flags) continue;
+        int nb = (x.q_len + rm.P - 1) / rm.P;
+        if (blk < nb) {
+            seg = s;
+            qb = blk;
+            sg = x;
+            break;
+        }
+        blk -= nb;
+    }
+    if (seg < 0) return;
+    const bool splits = seg_splits(sg, qsplit, a.nsplit);
+    if (!splits && split > 0) return;
+    const int nsplit = splits ? a.nsplit : 1;
+
+    const int heads_here = min(rm.Gc, g - hc * rm.Gc);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r = wave * 32 + (lane & 31);
+    const int hl = r / rm.P, pos = r % rm.P;
+    const int j = qb * rm.P + pos;
+    const bool valid = hl < heads_here && j < sg.q_len;
+    const int h = hk * g + hc * rm.Gc + hl;
+    const int t = sg.q_start + j;
+
+    const int64_t base = (int64_t)sg.kv_end - sg.q_len;
+    const int64_t p_min = base + qb * rm.P;
+    const int64_t p_max = base + min(qb * rm.P + rm.P, sg.q_len) - 1;
+    const int64_t p_lane = valid ? base + j : p_max;
+
+    int64_t lo64 = sg.window > 0 ? p_min - sg.window + 1 : 0;
+    int64_t hi64 = sg.kv_end;
+    if (sg.causal && p_max + 1 < hi64) hi64 = p_max + 1;
+    if (lo64 < 0) lo64 = 0;
+    if (hi64 < lo64) hi64 = lo64;
+    int k_lo, k_hi;
+    split_range((int)lo64, (int)hi64, split, nsplit, &k_lo, &k_hi);
+
+    bf16x8 qf[D / 16];
+    load_q<D>(qf, a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid, a.negate);
+
+    RowState<D> st;
+    init_state<D>(st);
+    KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
+              a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R};
+    attend_range<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, Ks,
+                    Vt);
+
+    if (!splits) {
+        store_out<D>(st, a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1], valid);
+    } else {
+        int64_t row = (((int64_t)seg * qsplit + j) * a.Hq + h) * a.nsplit + split;
+        store_partial<D>(st, a.c, a.part_o + row * D, a.part_ml + row * 2, valid);
+    }
+}
+
+// Finish pass over packed rows: merge split partials, zero rows that no valid
+// segment covers, and record the error word of this workgroup's rows.
+template <int D>
+__global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
+    __shared__ int flags_sh;
+    const int g = a.Hq / a.Hkv;
+    const RowMap rm = row_map(g);
+    const int qsplit = varlen_qsplit(rm.P);
+    if (threadIdx.x == 0) flags_sh = 0;
+    __syncthreads();
+    int flags = 0;
+    if (blockIdx.x == 0 && threadIdx.x < a.S) flags |= read_segment(a, threadIdx.x).flags;
+    if (blockIdx.x == 0)
+        for (int s = 256 + threadIdx.x; s < a.S; s += 256) flags |= read_segment(a, s).flags;
+
+    constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
+    const int t0 = blockIdx.x * kFinishRows;
+    for (int tt = 0; tt < kFinishRows; ++tt) {
+        const int t = t0 + tt;
+        if (t >= a.T) break;
+        int owner = -1, count = 0;
+        Segment sg;
+        for (int s = 0; s < a.S; ++s) {
+            Segment x = read_segment(a, s);
+            if (x.flags) continue;
+            if (t >= x.q_start && t < x.q_start + x.q_len) {
+                if (owner < 0) {
+                    owner = s;
+                    sg = x;
+                }
+                ++count;
+            }
+        }
+        if (count > 1) flags |= ATTN_SEG_OVERLAP;
+        if (owner >= 0 && !seg_splits(sg, qsplit, a.nsplit)) continue;
+        for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
+            const int h = e / TPR, d0 = (e % TPR) * 4;
+            u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
+            if (owner < 0) {
+                *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
+            } else {
+                int64_t row = (((int64_t)owner * qsplit + (t - sg.q_start)) * a.Hq + h) * a.nsplit;
+                combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, a.nsplit, d0, orow);
+            }
+        }
+    }
+    if (flags) atomicOr(&flags_sh, flags);
+    __syncthreads();
+    if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh;
+}
+
+// ---------------------------------------------------------------- host side
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+struct DeviceInfo {
+    int cus;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+int device_info(DeviceInfo* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_HIP, "hipGetDevice failed");
+    std::call_once(g_dev_once[dev], [dev] {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        g_dev[dev].cus = cus;
+    });
+    if (g_dev[dev].cus <= 0) return fail(ATTN_ERR_HIP, "could not read the compute-unit count");
+    *out = g_dev[dev];
+    return ATTN_OK;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+constexpr int64_t kMaxOffset = (int64_t)1 << 62;
+
+// Largest element offset reachable through sizes/strides (strides >= 0).
+bool offset_ok(const int64_t* sizes, const int64_t* str, int n) {
+    __int128 m = 0;
+    for (int i = 0; i < n; ++i) {
+        if (sizes[i] <= 0) return true;
+        m += (__int128)(sizes[i] - 1) * str[i];
+    }
+    return m < kMaxOffset;
+}
+
+// Layout rules shared by every tensor argument: innermost stride 1, other
+// strides non-negative multiples of 8 elements, 16-byte aligned base.
+int check_layout(const char* name, const void* p, const int64_t* str, int n) {
+    if (str[n - 1] != 1)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: innermost stride %lld, only 1 is supported", name,
+                    (long long)str[n - 1]);
+    for (int i = 0; i < n - 1; ++i)
+        if (str[i] < 0 || str[i] % 8 != 0)
+            return fail(ATTN_ERR_UNSUPPORTED,
+                        "%s: stride[%d] = %lld is not a non-negative multiple of 8", name, i,
+                        (long long)str[i]);
+    if ((uintptr_t)p % 16 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: base pointer is not 16-byte aligned", name);
+    return ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Key splits of a prefill launch: enough workgroups to give every compute
+// unit two, with at least 1024 keys per split.
+int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int cus) {
+    int forced = env_int("ATTN_FORCE_SPLITS", 0);
+    RowMap rm = row_map(Hq / Hkv);
+    int64_t base = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks * B * Hkv;
+    int by_keys = (Lkv + 1023) / 1024;
+    if (by_keys < 1) by_keys = 1;
+    int ns;
+    if (forced > 0) {
+        ns = forced;
+    } else {
+        int64_t want = (2 * (int64_t)cus + base - 1) / (base > 0 ? base : 1);
+        ns = (int)(want < kMaxSplits ? want : kMaxSplits);
+        if (ns > by_keys) ns = by_keys;
+    }
+    if (ns < 1) ns = 1;
+    if (ns > kMaxSplits) ns = kMaxSplits;
+    return ns;
+}
+
+size_t prefill_ws_bytes(int B, int Hq, int Lq, int D, int nsplit) {
+    if (nsplit <= 1) return 0;
+    size_t rows = (size_t)nsplit * B * Hq * Lq;
+    return align256(rows * D * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+// Key splits of a varlen launch (segments with q_len <= qsplit only):
+// about 512 keys per split over the rows a column can hold.
+int varlen_splits(int rows) {
+    int forced = env_int("ATTN_FORCE_SPLITS", 0);
+    int ns = forced > 0 ? forced : (rows + 511) / 512;
+    if (ns < 1) ns = 1;
+    if (ns > kMaxSplits) ns = kMaxSplits;
+    return ns;
+}
+
+int varlen_finish_blocks(int T) { return T > 0 ? (T + kFinishRows - 1) / kFinishRows : 1; }
+
+size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
+    RowMap rm = row_map(Hq / Hkv);
+    int qsplit = varlen_qsplit(rm.P);
+    int ns = varlen_splits(rows);
+    size_t err = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
+    if (ns <= 1) return err;
+    size_t prow = (size_t)(S > 0 ? S : 0) * qsplit * Hq * ns;
+    return err + align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_last_error(void) { return g_err; }
+
+size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0 || Hq % Hkv != 0) return 0;
+    if (D != 64 && D != 128) return 0;
+    if (Lq == 0) return 0;
+    DeviceInfo di;
+    if (device_info(&di) != ATTN_OK) return 0;
+    return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, di.cus));
+}
+
+int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                        int Hkv, int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
+                        const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
+                        int64_t q_pos0, int window, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    clear_err();
+    if (!q || !k || !v || !out) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+    if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0)
+        return fail(ATTN_ERR_INVALID, "sizes must satisfy B,Hq,Hkv >= 1 and Lq,Lkv >= 0");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+    if (!(scale == scale) || isinf(scale)) return fail(ATTN_ERR_INVALID, "scale is not finite");
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only 64 and 128", D);
+    if (q_pos0 > kMaxOffset || q_pos0 < -kMaxOffset)
+        return fail(ATTN_ERR_INVALID, "q_pos0 out of range");
+    int st;
+    if ((st = check_layout("q", q, q_str, 4))) return st;
+    if ((st = check_layout("k", k, k_str, 4))) return st;
+    if ((st = check_layout("v", v, v_str, 4))) return st;
+    if ((st = check_layout("out", out, o_str, 4))) return st;
+    const int64_t qsz[4] = {B, Hq, Lq, D}, ksz[4] = {B, Hkv, Lkv, D};
+    if (!offset_ok(qsz, q_str, 4) || !offset_ok(ksz, k_str, 4) || !offset_ok(ksz, v_str, 4) ||
+        !offset_ok(qsz, o_str, 4))
+        return fail(ATTN_ERR_INVALID, "element offsets exceed 2^62");
+    if (Lq == 0) return ATTN_OK;
+
+    DeviceInfo di;
+    if ((st = device_info(&di))) return st;
+    const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, di.cus);
+    const size_t need = prefill_ws_bytes(B, Hq, Lq, D, nsplit);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && (uintptr_t)workspace % 256 != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+
+    PrefillArgs a;
+    a.q = (const u16*)q;
+    a.k = (const u16*)k;
+    a.v = (const u16*)v;
+    a.out = (u16*)out;
+    size_t prow = (size_t)nsplit * B * Hq * Lq;
+    a.part_o = need ? (float*)workspace : nullptr;
+    a.part_ml = need ? (float*)((char*)workspace + align256(prow * D * sizeof(float))) : nullptr;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Lq = Lq;
+    a.Lkv = Lkv;
+    a.window = window > 0 ? window : 0;
+    a.nsplit = nsplit;
+    a.c = fabsf(scale) * kLog2e;
+    a.negate = scale < 0.f;
+    a.q_pos0 = q_pos0;
+    for (int i = 0; i < 4; ++i) {
+        a.qs[i] = q_str[i];
+        a.ks[i] = k_str[i];
+        a.vs[i] = v_str[i];
+        a.os[i] = o_str[i];
+    }
+    RowMap rm = row_map(Hq / Hkv);
+    int64_t gx = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks;
+    int64_t gy = (int64_t)B * Hkv;
+    if (gx > 0x7fffffff || gy > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large (%lld x %lld)", (long long)gx,
+                    (long long)gy);
+    hipStream_t s = (hipStream_t)stream;
+    dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)nsplit);
+    if (D == 64)
+        hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed");
+    if (nsplit > 1) {
+        int64_t rows = (int64_t)B * Hq * Lq;
+        int per = 256 / (D / 4);
+        int64_t nb = (rows + per - 1) / per;
+        if (D == 64)
+            hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)nb), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)nb), dim3(256), 0, s, a);
+        if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch failed");
+    }
+    return ATTN_OK;
+}
+
+size_t attn_sdpa_varlen_workspace(int S, int T, int Hq, int Hkv, int D, int rows, int cols) {
+    if (S < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || rows < 1 || cols < 2) return 0;
+    if (D != 64 && D != 128) return 0;
+    return varlen_ws_bytes(S, T, Hq, Hkv, D, rows);
+}
+
+int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, void* out,
+                     const int32_t* seq_info, int S, const int32_t* seg_attr, int T, int Hq,
+                     int Hkv, int D, int rows, int cols, float scale, int causal, int window,
+                     int ring_rows, const int64_t q_str[3], const int64_t k_str[4],
+                     const int64_t v_str[4], const int64_t o_str[3], void* workspace,
+                     size_t ws_bytes, void* stream) {
+    clear_err();
+    if (!q || !k_store || !v_store || !out) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+    if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
+    if (S < 0 || T < 0 || Hq < 1 || Hkv < 1 || rows < 1 || cols < 2)
+        return fail(ATTN_ERR_INVALID,
+                    "sizes must satisfy S,T >= 0, Hq,Hkv,rows >= 1 and cols >= 2");
+    if (S > 0 && !seq_info) return fail(ATTN_ERR_INVALID, "null seq_info");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+    if ((int64_t)S > 2 * (int64_t)(cols - 1))
+        return fail(ATTN_ERR_INVALID, "S = %d exceeds 2 x (cols - 1) = %d segments", S,
+                    2 * (cols - 1));
+    if (!seg_attr && ring_rows > rows)
+        return fail(ATTN_ERR_INVALID, "ring_rows %d exceeds rows %d", ring_rows, rows);
+    if (!seg_attr && !causal && window > 0)
+        return fail(ATTN_ERR_INVALID, "a window needs causal attention");
+    if (!(scale == scale) || isinf(scale)) return fail(ATTN_ERR_INVALID, "scale is not finite");
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only 64 and 128", D);
+    int st;
+    if ((st = check_layout("q", q, q_str, 3))) return st;
+    if ((st = check_layout("k_store", k_store, k_str, 4))) return st;
+    if ((st = check_layout("v_store", v_store, v_str, 4))) return st;
+    if ((st = check_layout("out", out, o_str, 3))) return st;
+    if (seq_info && (uintptr_t)seq_info % 4 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "seq_info is not 4-byte aligned");
+    if (seg_attr && (uintptr_t)seg_attr % 4 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "seg_attr is not 4-byte aligned");
+    const int64_t qsz[3] = {T, Hq, D}, ssz[4] = {rows, cols, Hkv, D};
+    if (!offset_ok(qsz, q_str, 3) || !offset_ok(ssz, k_str, 4) || !offset_ok(ssz, v_str, 4) ||
+        !offset_ok(qsz, o_str, 3))
+        return fail(ATTN_ERR_INVALID, "element offsets exceed 2^62");
+    const size_t need = varlen_ws_bytes(S, T, Hq, Hkv, D, rows);
+    if (!workspace || ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    DeviceInfo di;
+    if ((st = device_info(&di))) return st;
+
+    const int nsplit = varlen_splits(rows);
+    RowMap rm = row_map(Hq / Hkv);
+    const int qsplit = varlen_qsplit(rm.P);
+    VarlenArgs a;
+    a.q = (const u16*)q;
+    a.k = (const u16*)k_store;
+    a.v = (const u16*)v_store;
+    a.out = (u16*)out;
+    a.seq_info = seq_info;
+    a.seg_attr = seg_attr;
+    a.err = (int32_t*)workspace;
+    size_t errb = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
+    size_t prow = (size_t)S * qsplit * Hq * nsplit;
+    a.part_o = nsplit > 1 ? (float*)((char*)workspace + errb) : nullptr;
+    a.part_ml = nsplit > 1 ? (float*)((char*)workspace + errb + align256(prow * D * sizeof(float)))
+                           : nullptr;
+    a.S = S;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.rows = rows;
+    a.cols = cols;
+    a.causal = causal ? 1 : 0;
+    a.window = window;
+    a.ring_rows = ring_rows;
+    a.nsplit = nsplit;
+    a.c = fabsf(scale) * kLog2e;
+    a.negate = scale < 0.f;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = q_str[i];
+        a.os[i] = o_str[i];
+    }
+    for (int i = 0; i < 4; ++i) {
+        a.ks[i] = k_str[i];
+        a.vs[i] = v_str[i];
+    }
+    hipStream_t s = (hipStream_t)stream;
+    int64_t gx = (int64_t)(T + rm.P - 1) / rm.P + S;
+    int64_t gy = (int64_t)Hkv * rm.hchunks;
+    if (gx > 0x7fffffff || gy > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
+    if (gx > 0 && T > 0 && S > 0) {
+        dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)nsplit);
+        if (D == 64)
+            hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(varlen_kernel<128>, grid, dim3(kThreads), 0, s, a);
+        if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen launch failed");
+    }
+    dim3 fgrid((unsigned)varlen_finish_blocks(T));
+    if (D == 64)
+        hipLaunchKernelGGL(varlen_finish_kernel<64>, fgrid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(varlen_finish_kernel<128>, fgrid, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen finish launch failed");
+    return ATTN_OK;
+}
+
+int attn_varlen_read_error(const void* workspace, int S, int T, void* stream, int32_t* err_out) {
+    clear_err();
+    if (!workspace || !err_out) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (S < 0 || T < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    (void)S;
+    int n = varlen_finish_blocks(T);
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(ATTN_ERR_HIP, "stream sync failed");
+    int32_t* host = (int32_t*)malloc(sizeof(int32_t) * n);
+    if (!host) return fail(ATTN_ERR_INVALID, "host allocation failed");
+    if (hipMemcpy(host, workspace, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess) {
+        free(host);
+        return fail(ATTN_ERR_HIP, "copy of the error word failed");
+    }
+    int32_t e = 0;
+    for (int i = 0; i < n; ++i) e |= host[i];
+    free(host);
+    *err_out = e;
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+/*
+ * attn.h -- C ABI of libattn.so: causal GQA prefill and varlen SDPA on
+ * MI355X (gfx950).
+ *
+ * Every tensor argument is a DEVICE pointer to caller-owned memory; the
+ * library allocates no device memory and keeps no per-call state.  Strides
+ * are in ELEMENTS.  Calls are asynchronous on the given HIP stream (NULL:
+ * the default stream) and return once the kernels are enqueued; a fault in
+ * a kernel surfaces at the caller's next synchronisation.  All entry points
+ * are thread-safe.  Device properties are read lazily on the first call that
+ * passes validation, never at load time.
+ *
+ * Tensors are bf16 (bfloat16 bits), accumulation is fp32, outputs are
+ * rounded to bf16 with round-to-nearest-even.
+ *
+ * Return value: an attn_status.  On anything but ATTN_OK nothing was
+ * enqueued and attn_last_error() describes the reason.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* null pointer, bad size, inconsistent arguments   */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid, but not a layout this library computes   */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
+    ATTN_ERR_HIP = 4          /* the HIP runtime refused a query or a launch     */
+} attn_status;
+
+/* Bits of the varlen error word (attn_varlen_read_error).  A flagged
+ * segment is not attended; its packed rows are zeroed like uncovered rows. */
+#define ATTN_SEG_QRANGE 1   /* q_start < 0, q_len < 0 or q_start + q_len > T      */
+#define ATTN_SEG_COL 2      /* col outside [0, cols-1): the last column is scratch */
+#define ATTN_SEG_KVEND 4    /* kv_end < 0, or kv_end > rows on flat storage        */
+#define ATTN_SEG_ATTR 8     /* seg_attr ring_rows > rows                           */
+#define ATTN_SEG_OVERLAP 16 /* a packed row claimed by two valid segments; the
+                               outputs of those rows are then unspecified          */
+
+/* Version of this ABI; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/* Thread-local, human-readable reason for the last non-OK return on this
+ * thread ("" if none).  The string stays valid until the next call. */
+const char *attn_last_error(void);
+
+/*
+ * Causal grouped-query attention prefill.
+ *
+ * Defines ("[CUDA] Use Triton TMA for long-context causal prefill",
+ * Summary and operator-level performance table): global causal GQA softmax
+ * attention of Lq prefill query rows against an Lkv-long key/value prefix,
+ * head dimensions 64 and 128, output written through its real strides, and
+ * a finite result for query rows that see no key.
+ *
+ *   q   [B, Hq,  Lq,  D]  bf16, strides q_str[4]
+ *   k,v [B, Hkv, Lkv, D]  bf16, strides k_str[4], v_str[4]
+ *   out [B, Hq,  Lq,  D]  bf16, strides o_str[4] (written, any B/H/L strides)
+ *
+ * Query head h reads key/value head h / (Hq / Hkv).  Query row i sits at
+ * absolute position q_pos0 + i (pass Lkv - Lq for end-aligned prefill) and
+ * sees key j iff 0 <= j < Lkv, j <= q_pos0 + i and, when window > 0,
+ * j > q_pos0 + i - window (window keys including its own position).
+ * o = sum_j softmax_j(scale * q.k_j) v_j over the visible keys; a row with
+ * no visible key is written as exact zeros.
+ *
+ * Layout rules (else ATTN_ERR_UNSUPPORTED): D in {64, 128}; innermost
+ * stride 1 on all four tensors; base pointers 16-byte aligned; every other
+ * stride a multiple of 8 elements.
+ * Sizes (else ATTN_ERR_INVALID): B, Hq, Hkv >= 1; Lq, Lkv >= 0; Hq % Hkv == 0;
+ * all element offsets below 2^62.  Lq == 0 enqueues nothing.
+ *
+ * workspace: device memory of at least attn_causal_prefill_workspace(...)
+ * bytes (may be NULL when that is 0), 256-byte aligned; it holds split
+ * partial results and must not be shared by calls in flight.
+ */
+size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D);
+
+int attn_causal_prefill(const void *q, const void *k, const void *v, void *out,
+                        int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                        const int64_t q_str[4], const int64_t k_str[4],
+                        const int64_t v_str[4], const int64_t o_str[4],
+                        int64_t q_pos0, int window,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Length-aware varlen SDPA over per-sequence KV columns.
+ *
+ * Defines ("[executorch][cuda] Add a length-aware Triton SDPA over
+ * per-sequence KV columns", description and the stacked commits on the
+ * batched-sequence manifest layout and the batched sequence cache): each
+ * resident sequence owns one column of a [rows, cols, Hkv, D] store whose
+ * last column is scratch; the device table seq_info Int32[S,4] =
+ * (q_start, q_len, col, kv_end) says which packed query rows belong to which
+ * column and how many keys that sequence holds (the step's own tokens
+ * included).  Query j of a segment sits at position kv_end - q_len + j.  A
+ * key at position k is stored at row (k mod R) of its column, where R is the
+ * segment's ring rows (ring storage) or rows (flat storage).
+ *
+ *   q        [T, Hq, D]           bf16 packed query rows, strides q_str[3]
+ *   k_store,
+ *   v_store  [rows, cols, Hkv, D] bf16, strides k_str[4], v_str[4]
+ *   out      [T, Hq, D]           bf16, strides o_str[3] (every row written)
+ *   seq_info [S, 4] int32, device, contiguous: (q_start, q_len, col, kv_end)
+ *   seg_attr [S, 3] int32, device, contiguous, nullable: per-segment
+ *            (causal, window, ring_rows); when NULL every segment takes the
+ *            call's causal / window / ring_rows.
+ *
+ * Visibility of key k for a query at position p: k < kv_end, k <= p when
+ * causal, k > p - window when window > 0.  ring_rows <= 0 means flat
+ * storage.  Packed rows in [0, T) that no valid segment covers are written
+ * as zeros, in the same call.  The host never reads seq_info / seg_attr:
+ * launch geometry depends only on (S, T, Hq, Hkv, D, rows, cols), so one
+ * captured graph serves any lengths written into the same buffers.
+ * Invalid segments are skipped, zeroed and reported in the error word.
+ *
+ * Layout rules as for prefill (else ATTN_ERR_UNSUPPORTED).  Sizes (else
+ * ATTN_ERR_INVALID): S >= 0, T >= 0, rows >= 1, cols >= 2,
+ * S <= 2 * (cols - 1), Hq % Hkv == 0, ring_rows <= rows, and no window on a
+ * non-causal call when seg_attr is NULL.
+ *
+ * workspace: at least attn_sdpa_varlen_workspace(...) bytes, 256-byte
+ * aligned; it holds the error word and split partials.
+ */
+size_t attn_sdpa_varlen_workspace(int S, int T, int Hq, int Hkv, int D, int rows, int cols);
+
+int attn_sdpa_varlen(const void *q, const void *k_store, const void *v_store, void *out,
+                     const int32_t *seq_info, int S, const int32_t *seg_attr,
+                     int T, int Hq, int Hkv, int D, int rows, int cols, float scale,
+                     int causal, int window, int ring_rows,
+                     const int64_t q_str[3], const int64_t k_str[4],
+                     const int64_t v_str[4], const int64_t o_str[3],
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Reads the error word of the last attn_sdpa_varlen call that used this
+ * workspace (an OR of ATTN_SEG_* bits, 0 when every segment was valid).
+ * Synchronises `stream` first.  The arguments (S, T) must be those of that
+ * call.
+ */
+int attn_varlen_read_error(const void *workspace, int S, int T, void *stream,
+                           int32_t *err_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

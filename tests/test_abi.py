@@ -1,0 +1,176 @@
+"""The C ABI on the CPU: the library loads, exports what include/attn.h
+declares, and validates its arguments before touching the GPU.
+
+No call here reaches a kernel: every case is rejected by host validation
+(or is a no-op), so these run without a GPU.  Where a case is INVALID for
+the library it must also be rejected by the oracle: both apply the same
+written rules, each with its own code.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import causal_gqa_prefill_flash_amd as attn
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x10000  # a 16-byte aligned fake device address; never dereferenced here
+
+
+def _lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from causal_gqa_prefill_flash_amd import build
+        build.build()
+    return attn.lib()
+
+
+def _s(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = _lib()
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.attn_abi_version() == 1
+
+
+def _prefill(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64, scale=0.125,
+             qs=None, ks=None, vs=None, os_=None, q_pos0=8, window=0):
+    L = _lib()
+    qs = qs or _s(Hq * Lq * D, Lq * D, D, 1)
+    ks = ks or _s(Hkv * Lkv * D, Lkv * D, D, 1)
+    vs = vs or _s(Hkv * Lkv * D, Lkv * D, D, 1)
+    os_ = os_ or _s(Hq * Lq * D, Lq * D, D, 1)
+    return L.attn_causal_prefill(q, k, v, out, B, Hq, Hkv, Lq, Lkv, D, scale, qs, ks, vs, os_,
+                                 q_pos0, window, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ATTN_ERR_INVALID),
+    (dict(out=None), attn.ATTN_ERR_INVALID),
+    (dict(B=0), attn.ATTN_ERR_INVALID),
+    (dict(Hq=0), attn.ATTN_ERR_INVALID),
+    (dict(Lq=-1), attn.ATTN_ERR_INVALID),
+    (dict(Lkv=-5), attn.ATTN_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID),
+    (dict(D=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(D=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(qs=_s(4 * 8 * 64, 8 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),   # inner stride
+    (dict(ks=_s(2 * 16 * 64, 16 * 64, 68, 1)), attn.ATTN_ERR_UNSUPPORTED),  # row not 16 B
+    (dict(vs=_s(2 * 16 * 64, -16 * 64, 64, 1)), attn.ATTN_ERR_UNSUPPORTED),  # negative
+    (dict(out=A + 8), attn.ATTN_ERR_UNSUPPORTED),                           # misaligned
+    (dict(k=A + 2), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(**kw) == code
+    assert attn.last_error() != ""
+
+
+def test_prefill_empty_query_is_a_noop():
+    assert _prefill(Lq=0) == attn.ATTN_OK
+    assert attn.last_error() == ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Lq=-1), dict(Hq=6, Hkv=4), dict(Lkv=-5)])
+def test_oracle_rejects_what_the_library_calls_invalid(kw):
+    assert _prefill(**kw) == attn.ATTN_ERR_INVALID
+    L = oracle._load()
+    B, Hq, Hkv, Lq, Lkv, D = (kw.get(n, d) for n, d in
+                              (("B", 1), ("Hq", 4), ("Hkv", 2), ("Lq", 8), ("Lkv", 16), ("D", 64)))
+    buf = torch.zeros(1 << 16, dtype=torch.int16).numpy()
+    out = torch.zeros(1 << 16, dtype=torch.float64).numpy()
+    st = (ctypes.c_int64 * 4)(64, 64, 64, 1)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    rc = L.oracle_prefill(p, p, p, out.ctypes.data_as(ctypes.c_void_p), B, Hq, Hkv, Lq, Lkv, D,
+                          0.1, st, st, st, 0, 0, None, 0, None)
+    assert rc == 1
+
+
+def _varlen(S=2, T=16, Hq=4, Hkv=2, D=64, rows=32, cols=3, causal=1, window=0, ring_rows=0,
+            seq_info=A, seg_attr=None, ws=A, ws_bytes=None, q=A, qs=None, ks=None):
+    L = _lib()
+    if ws_bytes is None:
+        ws_bytes = L.attn_sdpa_varlen_workspace(max(S, 0), max(T, 0), Hq, max(Hkv, 1), D,
+                                                max(rows, 1), max(cols, 2)) or 1 << 20
+    qs = qs or _s(Hq * D, D, 1)
+    ks = ks or _s(cols * Hkv * D, Hkv * D, D, 1)
+    return L.attn_sdpa_varlen(q, A, A, A, seq_info, S, seg_attr, T, Hq, Hkv, D, rows, cols,
+                              0.125, causal, window, ring_rows, qs, ks, ks, _s(Hq * D, D, 1),
+                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ATTN_ERR_INVALID),
+    (dict(seq_info=None), attn.ATTN_ERR_INVALID),
+    (dict(S=-1), attn.ATTN_ERR_INVALID),
+    (dict(T=-1), attn.ATTN_ERR_INVALID),
+    (dict(cols=1), attn.ATTN_ERR_INVALID),
+    (dict(rows=0), attn.ATTN_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID),
+    (dict(S=5, cols=3), attn.ATTN_ERR_INVALID),          # > 2 x (cols - 1)
+    (dict(ring_rows=33), attn.ATTN_ERR_INVALID),         # ring larger than the store
+    (dict(causal=0, window=4), attn.ATTN_ERR_INVALID),   # window without causality
+    (dict(D=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(qs=_s(4 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=_s(3 * 2 * 64, 2 * 64, 60, 1)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws=A + 64), attn.ATTN_ERR_WORKSPACE),          # not 256-byte aligned
+])
+def test_varlen_validation(kw, code):
+    assert _varlen(**kw) == code
+    assert attn.last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(S=5, cols=3), dict(ring_rows=33), dict(causal=0, window=4),
+                                dict(cols=1)])
+def test_oracle_rejects_what_the_library_calls_invalid_varlen(kw):
+    assert _varlen(**kw) == attn.ATTN_ERR_INVALID
+    S = kw.get("S", 2)
+    cols = kw.get("cols", 3)
+    rows = 32
+    q = torch.zeros(16, 4, 64, dtype=torch.bfloat16)
+    st = torch.zeros(rows, max(cols, 1), 2, 64, dtype=torch.bfloat16)
+    info = [(2 * i, 1, 0, 4) for i in range(S)]
+    with pytest.raises(oracle.OracleInvalid):
+        oracle.varlen(q, st, st, info, causal=kw.get("causal", 1), window=kw.get("window", 0),
+                      ring_rows=kw.get("ring_rows", 0))
+
+
+def test_varlen_workspace_grows_with_segments_and_rows():
+    L = _lib()
+    a = L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 128, 8192, 9)
+    b = L.attn_sdpa_varlen_workspace(16, 1727, 16, 2, 128, 8192, 17)
+    c = L.attn_sdpa_varlen_workspace(8, 4000, 16, 2, 128, 8192, 9)
+    assert 0 < a < b and a < c
+    assert a % 256 == 0
+    assert L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 96, 8192, 9) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.causal_prefill(q, q[:, :1], q[:, :1])
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
+    with pytest.raises(ImportError):
+        attn.lib()

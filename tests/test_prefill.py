@@ -1,0 +1,154 @@
+"""Parity of attn_causal_prefill (HIP, through the C ABI) with the fp64 oracle."""
+import math
+import os
+
+import pytest
+import torch
+
+import causal_gqa_prefill_flash_amd as attn
+import oracle
+from causal_gqa_prefill_flash_amd import synth
+from gpu_util import compare, dev, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, **kw):
+    out = attn.causal_prefill(q.to(dev()), k.to(dev()), v.to(dev()), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lkv,D,q_pos0,window", [
+    (1, 4, 1, 256, 256, 64, 0, 0),        # the tiny workload
+    (2, 8, 2, 300, 1000, 64, None, 0),    # ragged Lq and Lkv, end-aligned
+    (2, 8, 2, 300, 1000, 128, None, 0),
+    (1, 16, 2, 77, 3001, 128, None, 0),
+    (1, 6, 2, 130, 700, 64, None, 0),     # g = 3: rows of a block are 3 heads x 42 positions
+    (1, 4, 4, 200, 333, 128, 0, 0),       # MHA (g = 1)
+    (1, 32, 1, 40, 500, 64, None, 0),     # g = 32
+    (1, 8, 2, 257, 900, 128, None, 100),  # sliding window
+    (1, 8, 2, 129, 129, 64, 0, 1),        # window of one key: returns V rows
+    (1, 8, 2, 100, 400, 128, 37, 0),      # q_pos0 inside the prefix: late keys unseen
+    (1, 8, 2, 64, 200, 64, -20, 0),       # 20 rows see nothing
+    (1, 8, 2, 1, 5000, 128, None, 0),     # a single query row
+    (1, 8, 2, 33, 0, 64, None, 0),        # no keys
+])
+def test_prefill_matches_oracle(B, Hq, Hkv, Lq, Lkv, D, q_pos0, window):
+    say("prefill", B, Hq, Hkv, Lq, Lkv, D, q_pos0, window)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=20)
+    scale = 1.0 / math.sqrt(D)
+    if q_pos0 is None:
+        q_pos0 = Lkv - Lq
+    out = _run(q, k, v, scale=scale, q_pos0=q_pos0, window=window)
+    ref = oracle.prefill(q, k, v, scale, q_pos0=q_pos0, window=window)
+    compare(out, ref, "B%d Hq%d Hkv%d Lq%d Lkv%d D%d" % (B, Hq, Hkv, Lq, Lkv, D))
+    if q_pos0 < 0:
+        assert torch.count_nonzero(out[:, :, :-q_pos0]) == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+def test_forced_splits_match_oracle(D, splits, monkeypatch):
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
+    B, Hq, Hkv, Lq, Lkv = 1, 16, 2, 96, 4100
+    say("forced splits", splits, "D", D)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=21)
+    out = _run(q, k, v)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D))
+    compare(out, ref, "splits %d D %d" % (splits, D))
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
+def test_scale_sign_and_zero(scale):
+    say("scale", scale)
+    q, k, v = synth.prefill_inputs(1, 8, 2, 70, 300, 64, wid=22)
+    out = _run(q, k, v, scale=scale)
+    ref = oracle.prefill(q, k, v, scale)
+    compare(out, ref, "scale %g" % scale)
+
+
+def test_output_through_real_strides_and_canary():
+    B, Hq, Hkv, Lq, Lkv, D = 2, 8, 2, 90, 600, 128
+    say("strided outputs")
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=23)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D))
+    # BSHD storage viewed as BHSD
+    bshd = torch.full((B, Lq, Hq, D), 7.0, dtype=torch.bfloat16, device=dev())
+    attn.causal_prefill(q.to(dev()), k.to(dev()), v.to(dev()), out=bshd.transpose(1, 2))
+    torch.cuda.synchronize()
+    compare(bshd.transpose(1, 2), ref, "BSHD output")
+    # padded L-stride: the padding must keep its canary
+    pad = torch.full((B, Hq, Lq, D + 64), 3.0, dtype=torch.bfloat16, device=dev())
+    attn.causal_prefill(q.to(dev()), k.to(dev()), v.to(dev()), out=pad[..., :D])
+    torch.cuda.synchronize()
+    compare(pad[..., :D], ref, "padded output")
+    assert torch.all(pad[..., D:] == 3.0)
+    # strided inputs: Q as a BSHD view, K/V with padded rows
+    qb = q.transpose(1, 2).contiguous().to(dev()).transpose(1, 2)
+    kp = torch.zeros(B, Hkv, Lkv, D + 8, dtype=torch.bfloat16)
+    kp[..., :D] = k
+    out = attn.causal_prefill(qb, kp.to(dev())[..., :D], v.to(dev()))
+    torch.cuda.synchronize()
+    compare(out, ref, "strided inputs")
+
+
+def test_deterministic_and_masked_keys_do_not_matter():
+    B, Hq, Hkv, Lq, Lkv, D = 1, 8, 2, 128, 2000, 128
+    say("determinism / masked keys")
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=24)
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    q_pos0 = 1000  # rows sit at 1000..1127: keys from 1128 on are never visible
+    a = attn.causal_prefill(qd, kd, vd, q_pos0=q_pos0).clone()
+    b = attn.causal_prefill(qd, kd, vd, q_pos0=q_pos0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    # NaN in keys no row can see
+    k2, v2 = kd.clone(), vd.clone()
+    k2[:, :, 1128:] = float("nan")
+    v2[:, :, 1128:] = float("nan")
+    c = attn.causal_prefill(qd, k2, v2, q_pos0=q_pos0)
+    # finite changes to a key that only later rows of a block see
+    k3, v3 = kd.clone(), vd.clone()
+    k3[:, :, 1127] += 5.0
+    v3[:, :, 1127] -= 3.0
+    d = attn.causal_prefill(qd, k3, v3, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(c, a)
+    assert torch.equal(d[:, :, :127], a[:, :, :127])
+    assert not torch.equal(d[:, :, 127], a[:, :, 127])
+
+
+# ------------------------------------------------------------- full-size workloads
+
+FULL = ["d64_lq512_lkv16k", "d128_lq1k_lkv128k", "d128_lq1k_lkv128k_masked16",
+        "d64_lq4k_lkv128k", "d128_lq4k_lkv128k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_on_sampled_rows(name):
+    w = synth.PREFILL_WORKLOADS[name]
+    B, Hq, Hkv, D, Lq, Lkv = w["B"], w["Hq"], w["Hkv"], w["D"], w["Lq"], w["Lkv"]
+    q_pos0 = w["q_pos0"] if w["q_pos0"] is not None else Lkv - Lq
+    say("full size", name)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=w["wid"])
+    out = _run(q, k, v, q_pos0=q_pos0)
+    rows = sample_rows(Lq, head=24, tail=24, every=211)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D), q_pos0=q_pos0, rows=rows)
+    compare(out[:, :, rows], ref, name)
+    if q_pos0 < 0:
+        z = out[:, :, : -q_pos0]
+        assert torch.count_nonzero(z) == 0 and torch.isfinite(out).all()
+
+
+def test_full_size_strided_output():
+    w = synth.PREFILL_WORKLOADS["d128_lq4k_lkv128k"]
+    B, Hq, Hkv, D, Lq, Lkv = w["B"], w["Hq"], w["Hkv"], w["D"], w["Lq"], w["Lkv"]
+    say("full size, BSHD output")
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=w["wid"])
+    bshd = torch.empty((B, Lq, Hq, D), dtype=torch.bfloat16, device=dev())
+    attn.causal_prefill(q.to(dev()), k.to(dev()), v.to(dev()), out=bshd.transpose(1, 2))
+    torch.cuda.synchronize()
+    rows = sample_rows(Lq, head=8, tail=8, every=509)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D), rows=rows)
+    compare(bshd.transpose(1, 2)[:, :, rows], ref, "BSHD full size")

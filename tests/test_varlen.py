@@ -1,0 +1,163 @@
+"""Parity of attn_sdpa_varlen (HIP, through the C ABI) with the fp64 oracle."""
+import math
+
+import pytest
+import torch
+
+import causal_gqa_prefill_flash_amd as attn
+import oracle
+from causal_gqa_prefill_flash_amd import synth
+from gpu_util import compare, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_varlen(q, ks, vs, seq_info, seg_attr=None, canary=float("nan"), **kw):
+    out = torch.full(q.shape, canary, dtype=torch.bfloat16, device=dev())
+    sa = seg_attr.to(dev()) if seg_attr is not None else None
+    si = seq_info.to(dev())
+    out, ws = attn.sdpa_varlen(q.to(dev()), ks.to(dev()), vs.to(dev()), si, seg_attr=sa,
+                               out=out, **kw)
+    err = attn.varlen_read_error(ws, si.shape[0], q.shape[0])
+    return out, err
+
+
+def test_pinned_table_matches_oracle():
+    say("varlen pinned table")
+    st = synth.VARLEN_STORE
+    info, attr, T = synth.pinned_varlen_table()
+    q, ks, vs = synth.varlen_inputs(T, st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"])
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == 0
+    compare(out, ref, "pinned table")
+    covered = torch.zeros(T, dtype=torch.bool)
+    for s in range(info.shape[0]):
+        covered[info[s, 0]: info[s, 0] + info[s, 1]] = True
+    assert int((~covered).sum()) == 41
+    assert torch.count_nonzero(out[(~covered).to(dev())]) == 0
+
+
+@pytest.mark.parametrize("seed", [5001, 5002, 5003, 5004])
+def test_seeded_tables_match_oracle(seed):
+    say("varlen seeded table", seed)
+    st = synth.VARLEN_STORE
+    info, attr, T = synth.random_varlen_table(seed)
+    q, ks, vs = synth.varlen_inputs(T, st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"],
+                                    wid=seed)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
+    assert err == 0
+    compare(out, ref, "seed %d" % seed)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_short_query_steps_split_keys(D):
+    """Every segment a decode-like step over a full column (the split path)."""
+    say("varlen short steps D", D)
+    rows, cols, Hkv, Hq = 8192, 9, 2, 16
+    qlens = [1, 4, 16, 1, 4, 16, 1, 16]
+    info, t = [], 0
+    for s, ql in enumerate(qlens):
+        info.append((t, ql, s, 8192 - 37 * s))
+        t += ql + 1
+    T = t
+    info = torch.tensor(info, dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=40)
+    out, err = _gpu_varlen(q, ks, vs, info)
+    ref = oracle.varlen(q, ks, vs, info)
+    assert err == 0
+    compare(out, ref, "short steps D%d" % D)
+
+
+def test_single_segment_equals_prefill_on_the_column_view():
+    say("varlen vs prefill on a strided column")
+    rows, cols, Hkv, D, Hq = 4096, 5, 2, 128, 16
+    q_len, kv_end, col = 200, 3333, 2
+    q, ks, vs = synth.varlen_inputs(q_len, rows, cols, Hkv, D, Hq, wid=41)
+    info = torch.tensor([(0, q_len, col, kv_end)], dtype=torch.int32)
+    out, err = _gpu_varlen(q, ks, vs, info)
+    assert err == 0
+    kd, vd, qd = ks.to(dev()), vs.to(dev()), q.to(dev())
+    kcol = kd[:kv_end, col].permute(1, 0, 2).unsqueeze(0)
+    vcol = vd[:kv_end, col].permute(1, 0, 2).unsqueeze(0)
+    pre = attn.causal_prefill(qd.permute(1, 0, 2).unsqueeze(0), kcol, vcol,
+                              q_pos0=kv_end - q_len)
+    torch.cuda.synchronize()
+    ref = oracle.varlen(q, ks, vs, info)
+    compare(out, ref, "varlen single segment")
+    compare(pre[0].permute(1, 0, 2), ref, "prefill on the column view")
+
+
+def test_unread_storage_does_not_matter():
+    """NaN in the scratch column, other columns, rows past kv_end and stale
+    ring rows leaves every output bit unchanged."""
+    say("varlen unread storage")
+    st = synth.VARLEN_STORE
+    info, attr, T = synth.pinned_varlen_table()
+    q, ks, vs = synth.varlen_inputs(T, st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"])
+    base, _ = _gpu_varlen(q, ks, vs, info, attr)
+    ks2, vs2 = ks.clone(), vs.clone()
+    nan = float("nan")
+    ks2[:, st["cols"] - 1] = nan            # scratch column
+    vs2[:, st["cols"] - 1] = nan
+    ks2[700:, 0] = nan                      # s1 (col 0) holds 700 keys
+    vs2[3000:, 1] = nan                     # s3 (col 1) holds 3000 keys
+    ks2[64:, 5] = nan                       # s2 (col 5) holds 64 keys
+    ks2[2559:, 4] = nan                     # ring column of s6: rows past the ring
+    vs2[2559:, 4] = nan
+    ks2[2000:, 6] = nan                     # s7's ring (col 6) holds positions 0..1999
+    ks2[:, 8] = nan
+    out, err = _gpu_varlen(q, ks2, vs2, info, attr)
+    assert err == 0
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_invalid_segments_are_flagged_and_zeroed():
+    say("varlen invalid segments")
+    rows, cols, Hkv, D, Hq = 1024, 4, 2, 64, 8
+    T = 64
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=42)
+    info = torch.tensor([(0, 8, 3, 100),      # scratch column
+                         (8, 8, 0, 2000),     # more keys than flat rows
+                         (60, 8, 1, 100),     # runs past T
+                         (20, 10, 2, 500),    # valid
+                         (40, 4, 1, 64)],     # valid
+                        dtype=torch.int32)
+    out, err = _gpu_varlen(q, ks, vs, info)
+    ref, flags = oracle.varlen(q, ks, vs, info, return_flags=True)
+    assert err == flags == (attn.SEG_COL | attn.SEG_KVEND | attn.SEG_QRANGE)
+    compare(out, ref, "invalid segments")
+    assert torch.count_nonzero(out[:20]) == 0
+
+
+def test_overlapping_segments_are_flagged():
+    say("varlen overlap flag")
+    rows, cols, Hkv, D, Hq = 256, 3, 1, 64, 4
+    q, ks, vs = synth.varlen_inputs(16, rows, cols, Hkv, D, Hq, wid=43)
+    info = torch.tensor([(0, 8, 0, 100), (4, 8, 1, 100)], dtype=torch.int32)
+    _, err = _gpu_varlen(q, ks, vs, info)
+    assert err & attn.SEG_OVERLAP
+
+
+def test_empty_table_zeroes_every_row():
+    say("varlen empty table")
+    rows, cols, Hkv, D, Hq = 64, 2, 1, 128, 2
+    q, ks, vs = synth.varlen_inputs(9, rows, cols, Hkv, D, Hq, wid=44)
+    info = torch.zeros((0, 4), dtype=torch.int32)
+    out, err = _gpu_varlen(q, ks, vs, info)
+    assert err == 0 and torch.count_nonzero(out) == 0
+
+
+def test_call_level_modes_without_seg_attr():
+    say("varlen call-level ring/window")
+    rows, cols, Hkv, D, Hq = 600, 4, 2, 64, 8
+    q, ks, vs = synth.varlen_inputs(80, rows, cols, Hkv, D, Hq, wid=45)
+    info = torch.tensor([(0, 30, 0, 1500), (35, 1, 2, 900), (40, 33, 1, 33)], dtype=torch.int32)
+    out, err = _gpu_varlen(q, ks, vs, info, causal=1, window=200, ring_rows=300)
+    ref = oracle.varlen(q, ks, vs, info, causal=1, window=200, ring_rows=300)
+    assert err == 0
+    compare(out, ref, "call-level ring")
+    out2, _ = _gpu_varlen(q, ks, vs, info, causal=0)
+    ref2 = oracle.varlen(q, ks, vs, info, causal=0)
+    compare(out2, ref2, "call-level non-causal")
