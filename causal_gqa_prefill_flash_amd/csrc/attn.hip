@@ -769,10 +769,12 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
                         int64_t q_pos0, int window, void* workspace, size_t ws_bytes,
                         void* stream) {
     clear_err();
-    if (!q || !k || !v || !out) return fail(ATTN_ERR_INVALID, "null tensor pointer");
     if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0)
         return fail(ATTN_ERR_INVALID, "sizes must satisfy B,Hq,Hkv >= 1 and Lq,Lkv >= 0");
+    // empty tensors may come with null pointers
+    if ((Lq > 0 && (!q || !out)) || (Lkv > 0 && (!k || !v)))
+        return fail(ATTN_ERR_INVALID, "null tensor pointer");
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
     if (!(scale == scale) || isinf(scale)) return fail(ATTN_ERR_INVALID, "scale is not finite");
     if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only 64 and 128", D);
@@ -862,7 +864,8 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
                      const int64_t v_str[4], const int64_t o_str[3], void* workspace,
                      size_t ws_bytes, void* stream) {
     clear_err();
-    if (!q || !k_store || !v_store || !out) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+    if (!k_store || !v_store || (T > 0 && (!q || !out)))
+        return fail(ATTN_ERR_INVALID, "null tensor pointer");
     if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
     if (S < 0 || T < 0 || Hq < 1 || Hkv < 1 || rows < 1 || cols < 2)
         return fail(ATTN_ERR_INVALID,

@@ -74,7 +74,8 @@ const char *attn_last_error(void);
  * stride 1 on all four tensors; base pointers 16-byte aligned; every other
  * stride a multiple of 8 elements.
  * Sizes (else ATTN_ERR_INVALID): B, Hq, Hkv >= 1; Lq, Lkv >= 0; Hq % Hkv == 0;
- * all element offsets below 2^62.  Lq == 0 enqueues nothing.
+ * all element offsets below 2^62; q/out non-null when Lq > 0 and k/v
+ * non-null when Lkv > 0.  Lq == 0 enqueues nothing; Lkv == 0 writes zeros.
  *
  * workspace: device memory of at least attn_causal_prefill_workspace(...)
  * bytes (may be NULL when that is 0), 256-byte aligned; it holds split
@@ -121,7 +122,8 @@ int attn_causal_prefill(const void *q, const void *k, const void *v, void *out,
  * Invalid segments are skipped, zeroed and reported in the error word.
  *
  * Layout rules as for prefill (else ATTN_ERR_UNSUPPORTED).  Sizes (else
- * ATTN_ERR_INVALID): S >= 0, T >= 0, rows >= 1, cols >= 2,
+ * ATTN_ERR_INVALID): non-null stores, q/out non-null when T > 0,
+ * S >= 0, T >= 0, rows >= 1, cols >= 2,
  * S <= 2 * (cols - 1), Hq % Hkv == 0, ring_rows <= rows, and no window on a
  * non-causal call when seg_attr is NULL.
  *

@@ -85,6 +85,10 @@ def test_prefill_validation(kw, code):
 def test_prefill_empty_query_is_a_noop():
     assert _prefill(Lq=0) == attn.ATTN_OK
     assert attn.last_error() == ""
+    # empty tensors may arrive as null pointers
+    assert _prefill(Lq=0, q=None, out=None) == attn.ATTN_OK
+    assert _prefill(Lkv=0, k=None, v=None, Lq=0) == attn.ATTN_OK
+    assert _prefill(Lkv=8, k=None) == attn.ATTN_ERR_INVALID
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Lq=-1), dict(Hq=6, Hkv=4), dict(Lkv=-5)])
