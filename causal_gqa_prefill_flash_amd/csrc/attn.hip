@@ -47,7 +47,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBM = kWaves * 32;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
-constexpr int kPad = 8;           // LDS row padding (elements): 16 bytes
 constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
 constexpr int kMaxSplits = 16;
 constexpr int kFinishRows = 4;    // packed rows per workgroup of the varlen finish pass
@@ -81,8 +80,11 @@ struct KVFlat {
     const u16* kb;
     const u16* vb;
     int64_t ks, vs;
-    __device__ const u16* krow(int j) const { return kb + (int64_t)j * ks; }
-    __device__ const u16* vrow(int j) const { return vb + (int64_t)j * vs; }
+    __device__ int row(int j) const { return j; }
+    __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
+    __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
+    // store row of key k0 + off, given base = row(k0)
+    __device__ int advance(int base, int off) const { return base + off; }
 };
 
 // Key/value rows of one column of a [rows, cols, H, D] store; position k
@@ -92,68 +94,96 @@ struct KVRing {
     const u16* vb;
     int64_t ks, vs;
     int R;
-    __device__ const u16* krow(int j) const { return kb + (int64_t)(j % R) * ks; }
-    __device__ const u16* vrow(int j) const { return vb + (int64_t)(j % R) * vs; }
-};
-
-template <int D>
-struct TileRegs {
-    static constexpr int kChunks = kBN * D / 8;  // 16-byte chunks of one K tile
-    static constexpr int kPer = kChunks / kThreads;
-    static constexpr int kVItems = (kBN / 4) * (D / 8);  // (4-key quad, 8-d chunk)
-    uint4 k[kPer];
-    uint4 v[4];
-};
-
-// Global -> registers: the K/V rows of keys [k0, k0+kBN); keys >= k_hi read as 0.
-template <int D, class KV>
-__device__ inline void load_tile(TileRegs<D>& t, const KV& kv, int k0, int k_hi, int tid) {
-#pragma unroll
-    for (int it = 0; it < TileRegs<D>::kPer; ++it) {
-        int c = tid + it * kThreads;
-        int key = c / (D / 8), d8 = c % (D / 8);
-        int j = k0 + key;
-        t.k[it] = j < k_hi ? ld16(kv.krow(j) + 8 * d8) : make_uint4(0, 0, 0, 0);
+    __device__ int row(int j) const { return j % R; }
+    __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
+    __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
+    __device__ int advance(int base, int off) const {
+        int r = base + off;
+        while (r >= R) r -= R;
+        return r;
     }
-    if (tid < TileRegs<D>::kVItems) {
-        int quad = tid % (kBN / 4), d8 = tid / (kBN / 4);
+};
+
+// LDS tiles hold K and V in their natural [key][d] order, 16-byte chunks of
+// each row XOR-swizzled so that the MFMA operand reads (ds_read_b128 for K,
+// ds_read_b64_tr_b16 for V) hit distinct banks.  Chunk c of row r sits at
+// position c ^ swz(r).
+template <int D>
+__device__ __host__ constexpr int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
+
+// Enqueue global -> LDS copies of the K and V rows of keys [k0, k0 + kBN)
+// (keys at or past k_hi re-read the last key of the range; their scores are
+// masked).  Each wave instruction fills 1 KB of LDS: lane l's 16 bytes land at
+// chunk position (instruction * 64 + l), which holds logical chunk
+// pos ^ swz(row) of its row.
+template <int D, class KV>
+__device__ inline void issue_tile(const KV& kv, int k0, int k_hi, u16* Kd, u16* Vd) {
+    constexpr int CH = D / 8;                 // 16-byte chunks per row
+    constexpr int ROWS_PER_INSTR = 64 / CH;   // rows filled by one wave instruction
+    constexpr int INSTR = kBN / ROWS_PER_INSTR;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int base = kv.row(k0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            int j = k0 + 4 * quad + jj;
-            t.v[jj] = j < k_hi ? ld16(kv.vrow(j) + 8 * d8) : make_uint4(0, 0, 0, 0);
-        }
+    for (int it = wave; it < INSTR; it += kWaves) {
+        const int P = it * 64 + lane;
+        const int r = P / CH, c = (P % CH) ^ swz<D>(r);
+        const int off = k0 + r < k_hi ? r : k_hi - 1 - k0;
+        const int row = kv.advance(base, off);
+        __builtin_amdgcn_global_load_lds((glb_void*)(kv.krow_at(row) + 8 * c),
+                                         (lds_void*)(Kd + it * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)(kv.vrow_at(row) + 8 * c),
+                                         (lds_void*)(Vd + it * 512), 16, 0, 0);
     }
 }
 
-__device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// Wait for this wave's outstanding global -> LDS copies, then for every wave.
+__device__ inline void tile_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
 
-// Registers -> LDS: K as Ks[key][d]; V transposed as Vt[d][perm(key)].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// V^T operand of O^T += V^T P^T for d-tile dt and key chunk c4: lane l needs
+// V[key(l)][32*dt + l%32] for its 8 key slots; two transposing reads give 4
+// keys each (lanes 4j..4j+3 of a 16-lane group point at key j's 4 d values).
 template <int D>
-__device__ inline void store_tile(const TileRegs<D>& t, u16* Ks, u16* Vt, int tid) {
-    constexpr int KSTR = D + kPad, VSTR = kBN + kPad;
-#pragma unroll
-    for (int it = 0; it < TileRegs<D>::kPer; ++it) {
-        int c = tid + it * kThreads;
-        int key = c / (D / 8), d8 = c % (D / 8);
-        *reinterpret_cast<uint4*>(Ks + key * KSTR + 8 * d8) = t.k[it];
-    }
-    if (tid < TileRegs<D>::kVItems) {
-        int quad = tid % (kBN / 4), d8 = tid / (kBN / 4);
-        // keys 4*quad .. 4*quad+3 land at pos .. pos+3 within the permuted order
-        int pos = 16 * (quad >> 2) + 8 * (quad & 1) + 4 * ((quad >> 1) & 1);
-        const uint32_t* a = reinterpret_cast<const uint32_t*>(&t.v[0]);
-        const uint32_t* b = reinterpret_cast<const uint32_t*>(&t.v[1]);
-        const uint32_t* c2 = reinterpret_cast<const uint32_t*>(&t.v[2]);
-        const uint32_t* d2 = reinterpret_cast<const uint32_t*>(&t.v[3]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint2 even = make_uint2(lo_pair(a[m], b[m]), lo_pair(c2[m], d2[m]));
-            uint2 odd = make_uint2(hi_pair(a[m], b[m]), hi_pair(c2[m], d2[m]));
-            *reinterpret_cast<uint2*>(Vt + (8 * d8 + 2 * m) * VSTR + pos) = even;
-            *reinterpret_cast<uint2*>(Vt + (8 * d8 + 2 * m + 1) * VSTR + pos) = odd;
-        }
-    }
+__device__ inline bf16x8 v_frag(const u16* Vs, int dt, int c4, int lane) {
+    constexpr int CH = D / 8;
+    const int h = lane >> 5, dh = (lane >> 4) & 1, L = lane & 15;
+    const int j = L >> 2, q = L & 3;
+    const int c = 4 * dt + 2 * dh + (q >> 1);
+    const int r0 = 16 * c4 + 4 * h + j, r1 = r0 + 8;
+    const u16* p0 = Vs + r0 * D + 8 * (c ^ swz<D>(r0)) + 4 * (q & 1);
+    const u16* p1 = Vs + r1 * D + 8 * (c ^ swz<D>(r1)) + 4 * (q & 1);
+    (void)CH;
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// K operand of S^T = K Q^T for key subtile t and d step kk.
+template <int D>
+__device__ inline bf16x8 k_frag(const u16* Ks, int t, int kk, int lane) {
+    const int r = 32 * t + (lane & 31), c = 2 * kk + (lane >> 5);
+    return lds_frag(Ks + r * D + 8 * (c ^ swz<D>(r)));
+}
+
+__device__ inline float max_across_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float sum_across_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Per-lane online-softmax state of one query row (lanes l and l+32 share a row).
@@ -164,93 +194,112 @@ struct RowState {
     float l;           // this lane's share of the running sum
 };
 
-// Attend the keys [k_lo, k_hi) for the 32 rows of this wave.
+// One key tile (keys k0 .. k0+kBN-1 in LDS) for the 32 rows of this wave.
+template <int D>
+__device__ inline void compute_tile(const u16* Ks, const u16* Vs, int k0, int k_hi, int causal,
+                                    int window, int64_t p_lane, int64_t p_min, int64_t p_max,
+                                    const bf16x8* qf, float c, RowState<D>& st) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int hh = lane >> 5;
+
+    // S^T = K Q^T: 32 keys x 32 rows per MFMA output
+    f32x16 s[kBN / 32];
+#pragma unroll
+    for (int t = 0; t < kBN / 32; ++t) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, t, kk, lane), qf[kk], acc,
+                                                          0, 0, 0);
+        s[t] = acc;
+    }
+
+    const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
+                           (window > 0 && (int64_t)k0 <= p_max - window);
+    if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                bool vis = key < k_hi && (!causal || key <= p_lane) &&
+                           (window <= 0 || key > p_lane - window);
+                s[t][r] = vis ? s[t][r] : -INFINITY;
+            }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
+    mx = max_across_halves(mx);
+    const float m_new = __builtin_fmaxf(st.m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
+    const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m_use) * c);
+    st.m = m_new;
+    const float mc = m_use * c;
+
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < kBN / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
+            if (need_mask) p = s[t][r] == -INFINITY ? 0.f : p;
+            s[t][r] = p;
+            lsum += p;
+        }
+    st.l = st.l * alpha + lsum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
+    }
+
+    // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int c4 = 0; c4 < kBN / 16; ++c4) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[c4 >> 1][8 * (c4 & 1) + e];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(Vs, dt, c4, lane), pb,
+                                                               st.o[dt], 0, 0, 0);
+    }
+}
+
+// LDS of one workgroup: two stages of K and V tiles.
+template <int D>
+struct TileSmem {
+    u16* k0;
+    u16* v0;
+    u16* k1;
+    u16* v1;
+};
+
+// Attend the keys [k_lo, k_hi) for the 32 rows of this wave: tiles alternate
+// between the two LDS stages; the copy of tile t+1 runs while tile t is
+// computed, with one barrier per tile.
 //   p_lane: position of this lane's row; p_min/p_max: extreme positions of
 //   the workgroup's rows (for the per-tile mask decision).
 template <int D, class KV>
 __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
                              int64_t p_lane, int64_t p_min, int64_t p_max, const bf16x8* qf,
-                             float c, RowState<D>& st, u16* Ks, u16* Vt) {
-    constexpr int KSTR = D + kPad, VSTR = kBN + kPad;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int lr = lane & 31, hh = lane >> 5;
+                             float c, RowState<D>& st, const TileSmem<D>& sm) {
     if (k_lo >= k_hi) return;
-
-    TileRegs<D> regs;
-    load_tile<D>(regs, kv, k_lo, k_hi, tid);
-    for (int k0 = k_lo; k0 < k_hi; k0 += kBN) {
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile<D>(regs, Ks, Vt, tid);
-        __syncthreads();
-        if (k0 + kBN < k_hi) load_tile<D>(regs, kv, k0 + kBN, k_hi, tid);
-
-        // S^T = K Q^T: 32 keys x 32 rows per MFMA output
-        f32x16 s[kBN / 32];
-#pragma unroll
-        for (int t = 0; t < kBN / 32; ++t) {
-            f32x16 acc = {};
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    lds_frag(Ks + (32 * t + lr) * KSTR + 16 * kk + 8 * hh), qf[kk], acc, 0, 0, 0);
-            s[t] = acc;
-        }
-
-        const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
-                               (window > 0 && (int64_t)k0 <= p_max - window);
-        if (need_mask) {
-#pragma unroll
-            for (int t = 0; t < kBN / 32; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    bool vis = key < k_hi && (!causal || key <= p_lane) &&
-                               (window <= 0 || key > p_lane - window);
-                    s[t][r] = vis ? s[t][r] : -INFINITY;
-                }
-        }
-
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < kBN / 32; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(st.m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
-        const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m_use) * c);
-        st.m = m_new;
-        const float mc = m_use * c;
-
-        float lsum = 0.f;
-#pragma unroll
-        for (int t = 0; t < kBN / 32; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
-                if (need_mask) p = s[t][r] == -INFINITY ? 0.f : p;
-                s[t][r] = p;
-                lsum += p;
-            }
-        st.l = st.l * alpha + lsum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
-        }
-
-        // O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-        for (int c4 = 0; c4 < kBN / 16; ++c4) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[c4 >> 1][8 * (c4 & 1) + e];
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    lds_frag(Vt + (32 * dt + lr) * VSTR + 16 * c4 + 8 * hh), pb, st.o[dt], 0, 0,
-                    0);
-        }
+    const int ntiles = (k_hi - k_lo + kBN - 1) / kBN;
+    issue_tile<D>(kv, k_lo, k_hi, sm.k0, sm.v0);
+    for (int t = 0; t < ntiles; t += 2) {
+        tile_barrier();
+        if (t + 1 < ntiles) issue_tile<D>(kv, k_lo + (t + 1) * kBN, k_hi, sm.k1, sm.v1);
+        compute_tile<D>(sm.k0, sm.v0, k_lo + t * kBN, k_hi, causal, window, p_lane, p_min, p_max,
+                        qf, c, st);
+        if (t + 1 >= ntiles) break;
+        tile_barrier();
+        if (t + 2 < ntiles) issue_tile<D>(kv, k_lo + (t + 2) * kBN, k_hi, sm.k0, sm.v0);
+        compute_tile<D>(sm.k1, sm.v1, k_lo + (t + 1) * kBN, k_hi, causal, window, p_lane, p_min,
+                        p_max, qf, c, st);
     }
 }
 
@@ -280,7 +329,7 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 template <int D>
 __device__ inline void store_out(const RowState<D>& st, u16* orow, bool valid) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    float l = st.l + __shfl_xor(st.l, 32);
+    float l = sum_across_halves(st.l);
     float inv = l > 0.f ? 1.f / l : 0.f;
     if (!valid) return;
 #pragma unroll
@@ -300,7 +349,7 @@ template <int D>
 __device__ inline void store_partial(const RowState<D>& st, float c, float* po, float* pml,
                                      bool valid) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    float l = st.l + __shfl_xor(st.l, 32);
+    float l = sum_across_halves(st.l);
     if (!valid) return;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -346,22 +395,43 @@ struct PrefillArgs {
     float* part_o;   // [nsplit][B][Hq][Lq][D]
     float* part_ml;  // [nsplit][B][Hq][Lq][2]
     int B, Hq, Hkv, Lq, Lkv, window, nsplit;
+    int n_inner;  // q blocks x head chunks
     float c;  // |scale| * log2(e)
     int negate;
     int64_t q_pos0;
     int64_t qs[4], ks[4], vs[4], os[4];
 };
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  Map
+// linear id L to work item w so that each XCD receives a contiguous range of
+// work items (a bijection on [0, N)); consecutive work items share their
+// K/V range, so each XCD's L2 streams its own slice of K/V.
+__device__ inline int xcd_remap(int L, int N) {
+    constexpr int X = 8;
+    const int per = N / X, rem = N % X;
+    const int x = L % X, i = L / X;
+    return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+#define DECLARE_TILE_SMEM(D)                                              \
+    __shared__ __attribute__((aligned(1024))) u16 sk0[kBN * (D)];        \
+    __shared__ __attribute__((aligned(1024))) u16 sv0[kBN * (D)];        \
+    __shared__ __attribute__((aligned(1024))) u16 sk1[kBN * (D)];        \
+    __shared__ __attribute__((aligned(1024))) u16 sv1[kBN * (D)];        \
+    const TileSmem<D> sm{sk0, sv0, sk1, sv1}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) u16 Ks[kBN * (D + kPad)];
-    __shared__ __attribute__((aligned(16))) u16 Vt[D * (kBN + kPad)];
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+    DECLARE_TILE_SMEM(D);
 
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
-    const int qb = blockIdx.x / rm.hchunks, hc = blockIdx.x % rm.hchunks;
-    const int b = blockIdx.y / a.Hkv, hk = blockIdx.y % a.Hkv;
-    const int split = blockIdx.z;
+    // work item: outer (b, hk, split), inner (q block, head chunk)
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int inner = w % a.n_inner, outer = w / a.n_inner;
+    const int qb = inner / rm.hchunks, hc = inner % rm.hchunks;
+    const int split = outer % a.nsplit, bh = outer / a.nsplit;
+    const int b = bh / a.Hkv, hk = bh % a.Hkv;
     const int q0 = qb * rm.P;
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
 
@@ -392,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     init_state<D>(st);
     KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
               a.vs[2]};
-    attend_range<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, Ks, Vt);
+    attend_range<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
     if (a.nsplit == 1) {
         store_out<D>(st, a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2], valid);
@@ -501,9 +571,8 @@ __device__ inline bool seg_splits(const Segment& g, int qsplit, int nsplit) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
-    __shared__ __attribute__((aligned(16))) u16 Ks[kBN * (D + kPad)];
-    __shared__ __attribute__((aligned(16))) u16 Vt[D * (kBN + kPad)];
+__global__ __launch_bounds__(kThreads, 2) void varlen_kernel(VarlenArgs a) {
+    DECLARE_TILE_SMEM(D);
 
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
@@ -561,8 +630,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     init_state<D>(st);
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
               a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R};
-    attend_range<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, Ks,
-                    Vt);
+    attend_range<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
     if (!splits) {
         store_out<D>(st, a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1], valid);
@@ -826,13 +894,13 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
         a.os[i] = o_str[i];
     }
     RowMap rm = row_map(Hq / Hkv);
-    int64_t gx = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks;
-    int64_t gy = (int64_t)B * Hkv;
-    if (gx > 0x7fffffff || gy > 65535)
-        return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large (%lld x %lld)", (long long)gx,
-                    (long long)gy);
+    const int64_t n_inner = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks;
+    const int64_t nwg = n_inner * B * Hkv * nsplit;
+    if (nwg > 0x7fffffff)
+        return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large (%lld workgroups)", (long long)nwg);
+    a.n_inner = (int)n_inner;
     hipStream_t s = (hipStream_t)stream;
-    dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)nsplit);
+    dim3 grid((unsigned)nwg);
     if (D == 64)
         hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
     else
