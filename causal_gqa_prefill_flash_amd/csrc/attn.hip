@@ -75,12 +75,23 @@ __device__ inline bf16x8 lds_frag(const u16* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Key/value rows of a flat [.., L, D] tensor.
 struct KVFlat {
     const u16* kb;
     const u16* vb;
     int64_t ks, vs;
     __device__ int row(int j) const { return j; }
+    // rows of keys j .. j + n - 1 are consecutive store rows
+    __device__ bool contiguous(int j, int n) const { return true; }
     __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
     __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
     // store row of key k0 + off, given base = row(k0)
@@ -95,6 +106,7 @@ struct KVRing {
     int64_t ks, vs;
     int R;
     __device__ int row(int j) const { return j % R; }
+    __device__ bool contiguous(int j, int n) const { return j % R + n <= R; }
     __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
     __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
     __device__ int advance(int base, int off) const {
@@ -116,28 +128,60 @@ __device__ __host__ constexpr int swz(int r) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void glb_void;
 
-// Enqueue global -> LDS copies of the K and V rows of keys [k0, k0 + kBN)
-// (keys at or past k_hi re-read the last key of the range; their scores are
-// masked).  Each wave instruction fills 1 KB of LDS: lane l's 16 bytes land at
-// chunk position (instruction * 64 + l), which holds logical chunk
-// pos ^ swz(row) of its row.
+// Geometry of the global -> LDS tile copies.  Each wave instruction fills
+// 1 KB of LDS: lane l's 16 bytes land at chunk position (instruction * 64 + l),
+// which holds logical chunk (position ^ swz(row)) of its row.  Wave w issues
+// instructions w, w + kWaves, ...
+template <int D>
+struct CopyPlan {
+    static constexpr int CH = D / 8;                // 16-byte chunks per row
+    static constexpr int ROWS = 64 / CH;            // rows per wave instruction
+    static constexpr int INSTR = kBN / ROWS;        // wave instructions per tensor
+    static constexpr int PER_WAVE = INSTR / kWaves;
+    static __device__ int row(int i) {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        return (wave + i * kWaves) * ROWS + (threadIdx.x & (kWave - 1)) / CH;
+    }
+    static __device__ int chunk(int i) {
+        return ((threadIdx.x & (kWave - 1)) % CH) ^ swz<D>(row(i));
+    }
+    static __device__ int lds_off(int i) {  // elements
+        return (__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) + i * kWaves) * 512;
+    }
+};
+
+// Enqueue global -> LDS copies of the K and V rows of keys [k0, k0 + kBN);
+// keys at or past k_hi re-read the last key of the range (their scores are
+// masked).  ks2/vs2: row strides in bytes when a tile's rows span less than
+// 2^31 bytes (else 0: the per-row path is taken).
 template <int D, class KV>
-__device__ inline void issue_tile(const KV& kv, int k0, int k_hi, u16* Kd, u16* Vd) {
-    constexpr int CH = D / 8;                 // 16-byte chunks per row
-    constexpr int ROWS_PER_INSTR = 64 / CH;   // rows filled by one wave instruction
-    constexpr int INSTR = kBN / ROWS_PER_INSTR;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+__device__ inline void issue_tile(const KV& kv, int ks2, int vs2, int k0, int k_hi, u16* Kd,
+                                  u16* Vd) {
+    typedef CopyPlan<D> CP;
     const int base = kv.row(k0);
+    if (ks2 > 0 && vs2 > 0 && k0 + kBN <= k_hi && kv.contiguous(k0, kBN)) {
+        // full tile of consecutive rows: scalar tile base + 32-bit lane offset
+        const char* kt = reinterpret_cast<const char*>(kv.krow_at(base));
+        const char* vt = reinterpret_cast<const char*>(kv.vrow_at(base));
 #pragma unroll
-    for (int it = wave; it < INSTR; it += kWaves) {
-        const int P = it * 64 + lane;
-        const int r = P / CH, c = (P % CH) ^ swz<D>(r);
-        const int off = k0 + r < k_hi ? r : k_hi - 1 - k0;
-        const int row = kv.advance(base, off);
-        __builtin_amdgcn_global_load_lds((glb_void*)(kv.krow_at(row) + 8 * c),
-                                         (lds_void*)(Kd + it * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void*)(kv.vrow_at(row) + 8 * c),
-                                         (lds_void*)(Vd + it * 512), 16, 0, 0);
+        for (int i = 0; i < CP::PER_WAVE; ++i) {
+            const int r = CP::row(i), c16 = 16 * CP::chunk(i);
+            __builtin_amdgcn_global_load_lds((glb_void*)(kt + (uint32_t)(r * ks2 + c16)),
+                                             (lds_void*)(Kd + CP::lds_off(i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(vt + (uint32_t)(r * vs2 + c16)),
+                                             (lds_void*)(Vd + CP::lds_off(i)), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CP::PER_WAVE; ++i) {
+            const int r = CP::row(i), c = CP::chunk(i);
+            const int off = k0 + r < k_hi ? r : k_hi - 1 - k0;
+            const int row = kv.advance(base, off);
+            __builtin_amdgcn_global_load_lds((glb_void*)(kv.krow_at(row) + 8 * c),
+                                             (lds_void*)(Kd + CP::lds_off(i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(kv.vrow_at(row) + 8 * c),
+                                             (lds_void*)(Vd + CP::lds_off(i)), 16, 0, 0);
+        }
     }
 }
 
@@ -164,8 +208,8 @@ __device__ inline bf16x8 v_frag(const u16* Vs, int dt, int c4, int lane) {
     (void)CH;
     s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
     s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    typedef long long i64x2 __attribute__((ext_vector_type(2)));
+    i64x2 ab = {__builtin_bit_cast(long long, a), __builtin_bit_cast(long long, b)};
     return __builtin_bit_cast(bf16x8, ab);
 }
 
@@ -194,63 +238,97 @@ struct RowState {
     float l;           // this lane's share of the running sum
 };
 
+// Visible keys of this lane's row inside the range [k_lo, k_hi): the
+// interval lo .. lo + span (span < 0: none), in int32.
+struct LaneBounds {
+    int lo;
+    int span;
+};
+
+__device__ inline LaneBounds lane_bounds(int k_lo, int k_hi, int causal, int window,
+                                         int64_t p_lane) {
+    int64_t hi = k_hi - 1;
+    if (causal && p_lane < hi) hi = p_lane;
+    int64_t lo = k_lo;
+    if (window > 0 && p_lane - window + 1 > lo) lo = p_lane - window + 1;
+    LaneBounds b;
+    if (hi < lo) {
+        b.lo = k_hi + (1 << 20);  // every key of the range lies below lo
+        b.span = 0;
+    } else {
+        b.lo = (int)lo;
+        b.span = (int)(hi - lo);
+    }
+    return b;
+}
+
 // One key tile (keys k0 .. k0+kBN-1 in LDS) for the 32 rows of this wave.
-template <int D>
-__device__ inline void compute_tile(const u16* Ks, const u16* Vs, int k0, int k_hi, int causal,
-                                    int window, int64_t p_lane, int64_t p_min, int64_t p_max,
+// MASK: the tile straddles a causal, window or range edge of some row.
+template <int D, bool MASK>
+__device__ inline void compute_tile(const u16* Ks, const u16* Vs, int k0, LaneBounds lb,
                                     const bf16x8* qf, float c, RowState<D>& st) {
     const int lane = threadIdx.x & (kWave - 1);
     const int hh = lane >> 5;
 
-    // S^T = K Q^T: 32 keys x 32 rows per MFMA output
-    f32x16 s[kBN / 32];
+    // S^T = K Q^T: two independent 32-key accumulators, interleaved
+    f32x16 s0 = {}, s1 = {};
 #pragma unroll
-    for (int t = 0; t < kBN / 32; ++t) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, t, kk, lane), qf[kk], acc,
-                                                          0, 0, 0);
-        s[t] = acc;
+    for (int kk = 0; kk < D / 16; ++kk) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, 0, kk, lane), qf[kk], s0, 0, 0,
+                                                     0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, 1, kk, lane), qf[kk], s1, 0, 0,
+                                                     0);
     }
+    f32x16 s[2] = {s0, s1};
 
-    const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
-                           (window > 0 && (int64_t)k0 <= p_max - window);
-    if (need_mask) {
+    if (MASK) {
+        // key k0 + 32t + 8(r/4) + 4hh + r%4 is visible iff 0 <= key - lo <= span
+        const unsigned base = (unsigned)(k0 + 4 * hh - lb.lo);
+        const unsigned span = (unsigned)lb.span;
 #pragma unroll
-        for (int t = 0; t < kBN / 32; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                int64_t key = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                bool vis = key < k_hi && (!causal || key <= p_lane) &&
-                           (window <= 0 || key > p_lane - window);
-                s[t][r] = vis ? s[t][r] : -INFINITY;
+                unsigned d = base + (unsigned)(32 * t + 8 * (r >> 2) + (r & 3));
+                s[t][r] = d <= span ? s[t][r] : -INFINITY;
             }
     }
 
-    float mx = -INFINITY;
+    float mx = st.m;
 #pragma unroll
-    for (int t = 0; t < kBN / 32; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
-    mx = max_across_halves(mx);
-    const float m_new = __builtin_fmaxf(st.m, mx);
+    const float m_new = max_across_halves(mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
     const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m_use) * c);
     st.m = m_new;
     const float mc = m_use * c;
 
-    float lsum = 0.f;
+    // P = 2^(s*c - m*c), rounded to bf16 pairs: the MFMA operand and the row sum
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    uint32_t pk[2][8];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < kBN / 32; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
-            if (need_mask) p = s[t][r] == -INFINITY ? 0.f : p;
-            s[t][r] = p;
-            lsum += p;
+        for (int r = 0; r < 16; r += 2) {
+            float x0 = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
+            float x1 = __builtin_amdgcn_exp2f(fmaf(s[t][r + 1], c, -mc));
+            if (MASK) {
+                x0 = s[t][r] == -INFINITY ? 0.f : x0;
+                x1 = s[t][r + 1] == -INFINITY ? 0.f : x1;
+            }
+            uint32_t w = pack_bf16x2(x0, x1);
+            pk[t][r >> 1] = w;
+            if (r & 2)
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ls1,
+                                                      false);
+            else
+                ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ls0,
+                                                      false);
         }
-    st.l = st.l * alpha + lsum;
+    st.l = st.l * alpha + (ls0 + ls1);
     if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
@@ -259,14 +337,26 @@ __device__ inline void compute_tile(const u16* Ks, const u16* Vs, int k0, int k_
     // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
     for (int c4 = 0; c4 < kBN / 16; ++c4) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[c4 >> 1][8 * (c4 & 1) + e];
+        const uint32_t* w = &pk[c4 >> 1][4 * (c4 & 1)];
+        uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
             st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(Vs, dt, c4, lane), pb,
                                                                st.o[dt], 0, 0, 0);
     }
+}
+
+template <int D>
+__device__ inline void tile_dispatch(const u16* Ks, const u16* Vs, int k0, int k_hi, int causal,
+                                     int window, int64_t p_min, int64_t p_max, LaneBounds lb,
+                                     const bf16x8* qf, float c, RowState<D>& st) {
+    const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
+                           (window > 0 && (int64_t)k0 <= p_max - window);
+    if (need_mask)
+        compute_tile<D, true>(Ks, Vs, k0, lb, qf, c, st);
+    else
+        compute_tile<D, false>(Ks, Vs, k0, lb, qf, c, st);
 }
 
 // LDS of one workgroup: two stages of K and V tiles.
@@ -289,17 +379,23 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
                              float c, RowState<D>& st, const TileSmem<D>& sm) {
     if (k_lo >= k_hi) return;
     const int ntiles = (k_hi - k_lo + kBN - 1) / kBN;
-    issue_tile<D>(kv, k_lo, k_hi, sm.k0, sm.v0);
+    const LaneBounds lb = lane_bounds(k_lo, k_hi, causal, window, p_lane);
+    // byte strides for the 32-bit per-lane copy offsets of full tiles
+    const int ks2 = kv.ks * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.ks * 2) : 0;
+    const int vs2 = kv.vs * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.vs * 2) : 0;
+    issue_tile<D>(kv, ks2, vs2, k_lo, k_hi, sm.k0, sm.v0);
+    // unrolled by two so that each stage is a distinct LDS object: the copy
+    // into one stage then never forces a wait before reads of the other
     for (int t = 0; t < ntiles; t += 2) {
         tile_barrier();
-        if (t + 1 < ntiles) issue_tile<D>(kv, k_lo + (t + 1) * kBN, k_hi, sm.k1, sm.v1);
-        compute_tile<D>(sm.k0, sm.v0, k_lo + t * kBN, k_hi, causal, window, p_lane, p_min, p_max,
-                        qf, c, st);
+        if (t + 1 < ntiles) issue_tile<D>(kv, ks2, vs2, k_lo + (t + 1) * kBN, k_hi, sm.k1, sm.v1);
+        tile_dispatch<D>(sm.k0, sm.v0, k_lo + t * kBN, k_hi, causal, window, p_min, p_max, lb, qf,
+                         c, st);
         if (t + 1 >= ntiles) break;
         tile_barrier();
-        if (t + 2 < ntiles) issue_tile<D>(kv, k_lo + (t + 2) * kBN, k_hi, sm.k0, sm.v0);
-        compute_tile<D>(sm.k1, sm.v1, k_lo + (t + 1) * kBN, k_hi, causal, window, p_lane, p_min,
-                        p_max, qf, c, st);
+        if (t + 2 < ntiles) issue_tile<D>(kv, ks2, vs2, k_lo + (t + 2) * kBN, k_hi, sm.k0, sm.v0);
+        tile_dispatch<D>(sm.k1, sm.v1, k_lo + (t + 1) * kBN, k_hi, causal, window, p_min, p_max,
+                         lb, qf, c, st);
     }
 }
 
@@ -318,11 +414,6 @@ __device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, bool nega
         u.w ^= flip;
         qf[kk] = __builtin_bit_cast(bf16x8, u);
     }
-}
-
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(u16, x) | ((uint32_t)__builtin_bit_cast(u16, y) << 16);
 }
 
 // Final normalisation and bf16 store of this lane's row: o / l, 0 when l == 0.
