@@ -218,6 +218,19 @@ def bench_varlen(args, name):
     }
 
 
+def calibrate_copy():
+    """A plain device copy of known size (256 MiB read, 256 MiB written),
+    three times, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 256 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +238,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="d128_lq1k_lkv128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a 256 MiB copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -233,6 +248,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.workload.startswith("varlen"):
         line = bench_varlen(args, args.workload)
     else:

@@ -48,8 +48,8 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kBM = kWaves * 32;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
-constexpr int kMaxSplits = 16;
-constexpr int kFinishRows = 4;    // packed rows per workgroup of the varlen finish pass
+constexpr int kMaxSplits = 16;    // key splits of a prefill launch
+constexpr int kMaxVarlenSplits = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Rows of a workgroup: Gc query heads (of one GQA group) x P positions.
@@ -564,30 +564,51 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 // Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
-// o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).
+// o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).  The splits are
+// read in groups of 8 whose loads are all in flight together (indices past
+// nsplit are clamped and weighted 0); groups merge by the same rule.
 template <int D>
 __device__ inline void combine_row(const float* po, const float* pml, int64_t split_stride_o,
                                    int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml[s * split_stride_ml]);
-    float L = 0.f;
+    constexpr int G = 8;
+    float M = -INFINITY, L = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            float ms = pml[s * split_stride_ml];
-            if (ms == -INFINITY) continue;
-            float w = __builtin_amdgcn_exp2f(ms - M);
-            L += w * pml[s * split_stride_ml + 1];
-            float4 x = *reinterpret_cast<const float4*>(po + s * split_stride_o + d0);
-            acc[0] += w * x.x;
-            acc[1] += w * x.y;
-            acc[2] += w * x.z;
-            acc[3] += w * x.w;
+    for (int s0 = 0; s0 < nsplit; s0 += G) {
+        float m[G], l[G];
+        float4 x[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int sj = min(s0 + j, nsplit - 1);
+            m[j] = pml[sj * split_stride_ml];
+            l[j] = pml[sj * split_stride_ml + 1];
+            x[j] = *reinterpret_cast<const float4*>(po + sj * split_stride_o + d0);
         }
+        float Mg = M;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (s0 + j < nsplit) Mg = __builtin_fmaxf(Mg, m[j]);
+        if (Mg == -INFINITY) continue;  // nothing visible so far
+        const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+        L *= r;
+        acc[0] *= r;
+        acc[1] *= r;
+        acc[2] *= r;
+        acc[3] *= r;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float w = (s0 + j < nsplit && m[j] != -INFINITY)
+                                ? __builtin_amdgcn_exp2f(m[j] - Mg) : 0.f;
+            L += w * l[j];
+            acc[0] += w * x[j].x;
+            acc[1] += w * x[j].y;
+            acc[2] += w * x[j].z;
+            acc[3] += w * x[j].w;
+        }
+        M = Mg;
     }
-    float inv = L > 0.f ? 1.f / L : 0.f;
-    uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                         pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
     *reinterpret_cast<uint2*>(orow + d0) = o;
 }
 
@@ -731,55 +752,53 @@ __global__ __launch_bounds__(kThreads, 2) void varlen_kernel(VarlenArgs a) {
     }
 }
 
-// Finish pass over packed rows: merge split partials, zero rows that no valid
-// segment covers, and record the error word of this workgroup's rows.
+// Finish pass, one packed row per workgroup: merge split partials, zero a
+// row that no valid segment covers, and record this workgroup's error word
+// (workgroup 0 also reports every segment's flags).
 template <int D>
 __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
-    __shared__ int flags_sh;
+    __shared__ int flags_sh, owner_sh, count_sh;
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
     const int qsplit = varlen_qsplit(rm.P);
-    if (threadIdx.x == 0) flags_sh = 0;
+    const int t = blockIdx.x;
+    if (threadIdx.x == 0) {
+        flags_sh = 0;
+        owner_sh = 0x7fffffff;
+        count_sh = 0;
+    }
     __syncthreads();
     int flags = 0;
-    if (blockIdx.x == 0 && threadIdx.x < a.S) flags |= read_segment(a, threadIdx.x).flags;
-    if (blockIdx.x == 0)
-        for (int s = 256 + threadIdx.x; s < a.S; s += 256) flags |= read_segment(a, s).flags;
-
-    constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
-    const int t0 = blockIdx.x * kFinishRows;
-    for (int tt = 0; tt < kFinishRows; ++tt) {
-        const int t = t0 + tt;
-        if (t >= a.T) break;
-        int owner = -1, count = 0;
-        Segment sg;
-        for (int s = 0; s < a.S; ++s) {
-            Segment x = read_segment(a, s);
-            if (x.flags) continue;
-            if (t >= x.q_start && t < x.q_start + x.q_len) {
-                if (owner < 0) {
-                    owner = s;
-                    sg = x;
-                }
-                ++count;
-            }
-        }
-        if (count > 1) flags |= ATTN_SEG_OVERLAP;
-        if (owner >= 0 && !seg_splits(sg, qsplit, a.nsplit)) continue;
-        for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
-            const int h = e / TPR, d0 = (e % TPR) * 4;
-            u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
-            if (owner < 0) {
-                *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
-            } else {
-                int64_t row = (((int64_t)owner * qsplit + (t - sg.q_start)) * a.Hq + h) * a.nsplit;
-                combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, a.nsplit, d0, orow);
-            }
+    for (int s = threadIdx.x; s < a.S; s += 256) {
+        const Segment x = read_segment(a, s);
+        if (blockIdx.x == 0) flags |= x.flags;
+        if (!x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len) {
+            atomicMin(&owner_sh, s);
+            atomicAdd(&count_sh, 1);
         }
     }
     if (flags) atomicOr(&flags_sh, flags);
     __syncthreads();
-    if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh;
+    if (t < a.T) {
+        const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
+        const Segment sg = owner >= 0 ? read_segment(a, owner) : Segment{};
+        if (owner < 0 || seg_splits(sg, qsplit, a.nsplit)) {
+            constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
+            for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
+                const int h = e / TPR, d0 = (e % TPR) * 4;
+                u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
+                if (owner < 0) {
+                    *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
+                } else {
+                    const int64_t row =
+                        (((int64_t)owner * qsplit + (t - sg.q_start)) * a.Hq + h) * a.nsplit;
+                    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, a.nsplit, d0,
+                                   orow);
+                }
+            }
+        }
+    }
+    if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh | (count_sh > 1 ? ATTN_SEG_OVERLAP : 0);
 }
 
 // ---------------------------------------------------------------- host side
@@ -884,16 +903,17 @@ size_t prefill_ws_bytes(int B, int Hq, int Lq, int D, int nsplit) {
 }
 
 // Key splits of a varlen launch (segments with q_len <= qsplit only):
-// about 512 keys per split over the rows a column can hold.
+// about 256 keys per split over the rows a column can hold.
 int varlen_splits(int rows) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
-    int ns = forced > 0 ? forced : (rows + 511) / 512;
+    int ns = forced > 0 ? forced : (rows + 255) / 256;
     if (ns < 1) ns = 1;
-    if (ns > kMaxSplits) ns = kMaxSplits;
+    if (ns > kMaxVarlenSplits) ns = kMaxVarlenSplits;
     return ns;
 }
 
-int varlen_finish_blocks(int T) { return T > 0 ? (T + kFinishRows - 1) / kFinishRows : 1; }
+// One finish workgroup (and error word) per packed row; one when T == 0.
+int varlen_finish_blocks(int T) { return T > 0 ? T : 1; }
 
 size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
     RowMap rm = row_map(Hq / Hkv);
