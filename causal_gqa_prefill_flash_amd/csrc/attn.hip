@@ -45,7 +45,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kBM = kWaves * 32;  // query rows per workgroup
+constexpr int kNT = 1;                  // 32-row MFMA tiles of query rows per wave
+constexpr int kBM = kWaves * 32 * kNT;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
 constexpr int kMaxSplits = 16;    // key splits of a prefill launch
@@ -150,37 +151,31 @@ struct CopyPlan {
     }
 };
 
-// Enqueue global -> LDS copies of the K and V rows of keys [k0, k0 + kBN);
-// keys at or past k_hi re-read the last key of the range (their scores are
-// masked).  ks2/vs2: row strides in bytes when a tile's rows span less than
-// 2^31 bytes (else 0: the per-row path is taken).
+// Enqueue global -> LDS copies of the rows of keys [k0, k0 + kBN) of one
+// tensor (K or V); keys at or past k_hi re-read the last key of the range
+// (their scores are masked).  rs2: row stride in bytes when a tile's rows
+// span less than 2^31 bytes (else 0: the per-row path is taken).
 template <int D, class KV>
-__device__ inline void issue_tile(const KV& kv, int ks2, int vs2, int k0, int k_hi, u16* Kd,
-                                  u16* Vd) {
+__device__ inline void issue_rows(const KV& kv, const u16* tb, int64_t rs, int rs2, int k0,
+                                  int k_hi, u16* dst) {
     typedef CopyPlan<D> CP;
     const int base = kv.row(k0);
-    if (ks2 > 0 && vs2 > 0 && k0 + kBN <= k_hi && kv.contiguous(k0, kBN)) {
+    if (rs2 > 0 && k0 + kBN <= k_hi && kv.contiguous(k0, kBN)) {
         // full tile of consecutive rows: scalar tile base + 32-bit lane offset
-        const char* kt = reinterpret_cast<const char*>(kv.krow_at(base));
-        const char* vt = reinterpret_cast<const char*>(kv.vrow_at(base));
+        const char* t = reinterpret_cast<const char*>(tb + (int64_t)base * rs);
 #pragma unroll
-        for (int i = 0; i < CP::PER_WAVE; ++i) {
-            const int r = CP::row(i), c16 = 16 * CP::chunk(i);
-            __builtin_amdgcn_global_load_lds((glb_void*)(kt + (uint32_t)(r * ks2 + c16)),
-                                             (lds_void*)(Kd + CP::lds_off(i)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(vt + (uint32_t)(r * vs2 + c16)),
-                                             (lds_void*)(Vd + CP::lds_off(i)), 16, 0, 0);
-        }
+        for (int i = 0; i < CP::PER_WAVE; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (glb_void*)(t + (uint32_t)(CP::row(i) * rs2 + 16 * CP::chunk(i))),
+                (lds_void*)(dst + CP::lds_off(i)), 16, 0, 0);
     } else {
 #pragma unroll
         for (int i = 0; i < CP::PER_WAVE; ++i) {
-            const int r = CP::row(i), c = CP::chunk(i);
+            const int r = CP::row(i);
             const int off = k0 + r < k_hi ? r : k_hi - 1 - k0;
             const int row = kv.advance(base, off);
-            __builtin_amdgcn_global_load_lds((glb_void*)(kv.krow_at(row) + 8 * c),
-                                             (lds_void*)(Kd + CP::lds_off(i)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(kv.vrow_at(row) + 8 * c),
-                                             (lds_void*)(Vd + CP::lds_off(i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void*)(tb + (int64_t)row * rs + 8 * CP::chunk(i)),
+                                             (lds_void*)(dst + CP::lds_off(i)), 16, 0, 0);
         }
     }
 }
@@ -230,16 +225,17 @@ __device__ inline float sum_across_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-lane online-softmax state of one query row (lanes l and l+32 share a row).
+// Per-lane online-softmax state of the wave's kNT query rows held by this
+// lane (lanes l and l+32 share a row).
 template <int D>
 struct RowState {
-    f32x16 o[D / 32];  // O^T accumulator: d = 32*dt + 8*(r/4) + 4*(lane/32) + r%4
-    float m;           // running maximum of raw scores (-inf: nothing seen)
-    float l;           // this lane's share of the running sum
+    f32x16 o[kNT][D / 32];  // O^T accumulators: d = 32*dt + 8*(r/4) + 4*(lane/32) + r%4
+    float m[kNT];           // running maximum of raw scores (-inf: nothing seen)
+    float l[kNT];           // this lane's share of the running sum
 };
 
-// Visible keys of this lane's row inside the range [k_lo, k_hi): the
-// interval lo .. lo + span (span < 0: none), in int32.
+// Visible keys of one row inside the range [k_lo, k_hi): the interval
+// lo .. lo + span, in int32.
 struct LaneBounds {
     int lo;
     int span;
@@ -262,101 +258,125 @@ __device__ inline LaneBounds lane_bounds(int k_lo, int k_hi, int causal, int win
     return b;
 }
 
-// One key tile (keys k0 .. k0+kBN-1 in LDS) for the 32 rows of this wave.
-// MASK: the tile straddles a causal, window or range edge of some row.
-template <int D, bool MASK>
-__device__ inline void compute_tile(const u16* Ks, const u16* Vs, int k0, LaneBounds lb,
-                                    const bf16x8* qf, float c, RowState<D>& st) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int hh = lane >> 5;
+// Scores of one key tile for the wave's rows: [row tile][32-key subtile].
+typedef f32x16 TileScores[kNT][2];
 
-    // S^T = K Q^T: two independent 32-key accumulators, interleaved
-    f32x16 s0 = {}, s1 = {};
+// S^T = K Q^T for one key tile (keys in LDS).  Each K fragment read from LDS
+// feeds the MFMAs of all kNT row tiles.
+template <int D>
+__device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileScores& s) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) s[nt][0] = s[nt][1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, 0, kk, lane), qf[kk], s0, 0, 0,
-                                                     0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(Ks, 1, kk, lane), qf[kk], s1, 0, 0,
-                                                     0);
+        const bf16x8 a0 = k_frag<D>(Ks, 0, kk, lane), a1 = k_frag<D>(Ks, 1, kk, lane);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            s[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[nt][kk], s[nt][0], 0, 0, 0);
+            s[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[nt][kk], s[nt][1], 0, 0, 0);
+        }
     }
-    f32x16 s[2] = {s0, s1};
+}
 
-    if (MASK) {
-        // key k0 + 32t + 8(r/4) + 4hh + r%4 is visible iff 0 <= key - lo <= span
-        const unsigned base = (unsigned)(k0 + 4 * hh - lb.lo);
-        const unsigned span = (unsigned)lb.span;
+// Scores of keys a row does not see become -inf: key k0 + 32t + 8(r/4) +
+// 4hh + r%4 is visible iff 0 <= key - lo <= span.
+__device__ inline void mask_tile(TileScores& s, int k0, const LaneBounds* lb) {
+    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const unsigned base = (unsigned)(k0 + 4 * hh - lb[nt].lo);
+        const unsigned span = (unsigned)lb[nt].span;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                unsigned d = base + (unsigned)(32 * t + 8 * (r >> 2) + (r & 3));
-                s[t][r] = d <= span ? s[t][r] : -INFINITY;
+                const unsigned d = base + (unsigned)(32 * t + 8 * (r >> 2) + (r & 3));
+                s[nt][t][r] = d <= span ? s[nt][t][r] : -INFINITY;
             }
     }
+}
 
-    float mx = st.m;
+// Running maxima after a tile: m_new = max(m, row max of s); alpha =
+// 2^((m - m_new) c) rescales what was accumulated against m (0 when nothing
+// was seen before).
+__device__ inline void update_max(const TileScores& s, float c, float* m, float* alpha) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int nt = 0; nt < kNT; ++nt) {
+        float mx = m[nt];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[t][r]);
-    const float m_new = max_across_halves(mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
-    const float alpha = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m - m_use) * c);
-    st.m = m_new;
-    const float mc = m_use * c;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[nt][t][r]);
+        const float m_new = max_across_halves(mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
+        alpha[nt] = m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[nt] - m_use) * c);
+        m[nt] = m_new;
+    }
+}
 
-    // P = 2^(s*c - m*c), rounded to bf16 pairs: the MFMA operand and the row sum
+// P = 2^(s c - m c) rounded to packed bf16 pairs (the B operand of the PV
+// MFMA); the row sums come from the rounded values.  Masked scores are -inf
+// and c > 0, so they give exactly 0.
+typedef uint32_t TileP[kNT][2][8];
+
+__device__ inline void softmax_tile(const TileScores& s, float c, const float* m, TileP& pk,
+                                    float* lsum) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    uint32_t pk[2][8];
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float mc = (m[nt] == -INFINITY ? 0.f : m[nt]) * c;
+        float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            float x0 = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mc));
-            float x1 = __builtin_amdgcn_exp2f(fmaf(s[t][r + 1], c, -mc));
-            if (MASK) {
-                x0 = s[t][r] == -INFINITY ? 0.f : x0;
-                x1 = s[t][r + 1] == -INFINITY ? 0.f : x1;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float x0 = __builtin_amdgcn_exp2f(fmaf(s[nt][t][r], c, -mc));
+                const float x1 = __builtin_amdgcn_exp2f(fmaf(s[nt][t][r + 1], c, -mc));
+                const uint32_t w = pack_bf16x2(x0, x1);
+                pk[nt][t][r >> 1] = w;
+                if (r & 2)
+                    ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                                          ls1, false);
+                else
+                    ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
+                                                          ls0, false);
             }
-            uint32_t w = pack_bf16x2(x0, x1);
-            pk[t][r >> 1] = w;
-            if (r & 2)
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ls1,
-                                                      false);
-            else
-                ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ls0,
-                                                      false);
-        }
-    st.l = st.l * alpha + (ls0 + ls1);
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
+        lsum[nt] = ls0 + ls1;
     }
+}
 
-    // O^T += V^T P^T, 16 keys per MFMA
+// O^T += V^T P^T for one key tile (V in LDS), 16 keys per MFMA; each V
+// fragment feeds the MFMAs of all kNT row tiles.
+template <int D>
+__device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st) {
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int c4 = 0; c4 < kBN / 16; ++c4) {
-        const uint32_t* w = &pk[c4 >> 1][4 * (c4 & 1)];
-        uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D>(Vs, dt, c4, lane), pb,
-                                                               st.o[dt], 0, 0, 0);
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const bf16x8 vf = v_frag<D>(Vs, dt, c4, lane);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const uint32_t* w = &pk[nt][c4 >> 1][4 * (c4 & 1)];
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+                st.o[nt][dt] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[nt][dt], 0, 0, 0);
+            }
+        }
     }
 }
 
 template <int D>
-__device__ inline void tile_dispatch(const u16* Ks, const u16* Vs, int k0, int k_hi, int causal,
-                                     int window, int64_t p_min, int64_t p_max, LaneBounds lb,
-                                     const bf16x8* qf, float c, RowState<D>& st) {
-    const bool need_mask = (k0 + kBN > k_hi) || (causal && (int64_t)k0 + kBN - 1 > p_min) ||
-                           (window > 0 && (int64_t)k0 <= p_max - window);
-    if (need_mask)
-        compute_tile<D, true>(Ks, Vs, k0, lb, qf, c, st);
-    else
-        compute_tile<D, false>(Ks, Vs, k0, lb, qf, c, st);
+__device__ inline void rescale(const float* alpha, RowState<D>& st) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        st.l[nt] *= alpha[nt];
+        if (__any(alpha[nt] != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] *= alpha[nt];
+        }
+    }
 }
 
 // LDS of one workgroup: two stages of K and V tiles.
@@ -368,39 +388,102 @@ struct TileSmem {
     u16* v1;
 };
 
-// Attend the keys [k_lo, k_hi) for the 32 rows of this wave: tiles alternate
+// Per-range constants of the key loop.
+template <class KV>
+struct KeyLoop {
+    KV kv;
+    int k_lo, k_hi, causal, window;
+    int64_t p_min, p_max;
+    int ks2, vs2;  // byte strides for the full-tile copy path (0: per-row path)
+    __device__ int k0(int t) const { return k_lo + t * kBN; }
+    // a tile straddles a causal, window or range edge of some row
+    __device__ bool needs_mask(int t) const {
+        const int a = k0(t);
+        return (a + kBN > k_hi) || (causal && (int64_t)a + kBN - 1 > p_min) ||
+               (window > 0 && (int64_t)a <= p_max - window);
+    }
+};
+
+template <int D, class KV>
+__device__ inline void copy_k(const KeyLoop<KV>& L, int t, u16* dst) {
+    issue_rows<D>(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.k0(t), L.k_hi, dst);
+}
+template <int D, class KV>
+__device__ inline void copy_v(const KeyLoop<KV>& L, int t, u16* dst) {
+    issue_rows<D>(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.k0(t), L.k_hi, dst);
+}
+
+// One key tile (K and V in LDS) for the rows of this wave.  Edge tiles
+// only add an in-place mask of the scores, so every tile runs the same code
+// and the accumulators keep their registers across the loop.
+template <int D, class KV>
+__device__ inline void tile_body(const KeyLoop<KV>& L, int t, const bf16x8 (*qf)[D / 16],
+                                 float c, const LaneBounds* lb, RowState<D>& st, const u16* Ks,
+                                 const u16* Vs) {
+    TileScores S;
+    qk_tile<D>(Ks, qf, S);
+    if (L.needs_mask(t)) mask_tile(S, L.k0(t), lb);
+    float alpha[kNT];
+    update_max(S, c, st.m, alpha);
+    rescale<D>(alpha, st);
+    TileP pk;
+    float lsum[kNT];
+    softmax_tile(S, c, st.m, pk, lsum);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) st.l[nt] += lsum[nt];
+    pv_tile<D>(Vs, pk, st);
+}
+
+// Attend the keys [k_lo, k_hi) for the rows of this wave: tiles alternate
 // between the two LDS stages; the copy of tile t+1 runs while tile t is
 // computed, with one barrier per tile.
-//   p_lane: position of this lane's row; p_min/p_max: extreme positions of
-//   the workgroup's rows (for the per-tile mask decision).
+//   p_lane[nt]: position of this lane's row in row tile nt; p_min/p_max:
+//   extreme positions of the workgroup's rows (for the per-tile mask
+//   decision).
 template <int D, class KV>
 __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
-                             int64_t p_lane, int64_t p_min, int64_t p_max, const bf16x8* qf,
-                             float c, RowState<D>& st, const TileSmem<D>& sm) {
+                             const int64_t* p_lane, int64_t p_min, int64_t p_max,
+                             const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
+                             const TileSmem<D>& sm) {
     if (k_lo >= k_hi) return;
-    const int ntiles = (k_hi - k_lo + kBN - 1) / kBN;
-    const LaneBounds lb = lane_bounds(k_lo, k_hi, causal, window, p_lane);
-    // byte strides for the 32-bit per-lane copy offsets of full tiles
-    const int ks2 = kv.ks * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.ks * 2) : 0;
-    const int vs2 = kv.vs * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.vs * 2) : 0;
-    issue_tile<D>(kv, ks2, vs2, k_lo, k_hi, sm.k0, sm.v0);
+    KeyLoop<KV> L;
+    L.kv = kv;
+    L.k_lo = k_lo;
+    L.k_hi = k_hi;
+    L.causal = causal;
+    L.window = window;
+    L.p_min = p_min;
+    L.p_max = p_max;
+    L.ks2 = kv.ks * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.ks * 2) : 0;
+    L.vs2 = kv.vs * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.vs * 2) : 0;
+    const int n = (k_hi - k_lo + kBN - 1) / kBN;
+    LaneBounds lb[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) lb[nt] = lane_bounds(k_lo, k_hi, causal, window, p_lane[nt]);
+
+    copy_k<D>(L, 0, sm.k0);
+    copy_v<D>(L, 0, sm.v0);
     // unrolled by two so that each stage is a distinct LDS object: the copy
     // into one stage then never forces a wait before reads of the other
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = 0; t < n; t += 2) {
         tile_barrier();
-        if (t + 1 < ntiles) issue_tile<D>(kv, ks2, vs2, k_lo + (t + 1) * kBN, k_hi, sm.k1, sm.v1);
-        tile_dispatch<D>(sm.k0, sm.v0, k_lo + t * kBN, k_hi, causal, window, p_min, p_max, lb, qf,
-                         c, st);
-        if (t + 1 >= ntiles) break;
+        if (t + 1 < n) {
+            copy_k<D>(L, t + 1, sm.k1);
+            copy_v<D>(L, t + 1, sm.v1);
+        }
+        tile_body<D>(L, t, qf, c, lb, st, sm.k0, sm.v0);
+        if (t + 1 >= n) break;
         tile_barrier();
-        if (t + 2 < ntiles) issue_tile<D>(kv, ks2, vs2, k_lo + (t + 2) * kBN, k_hi, sm.k0, sm.v0);
-        tile_dispatch<D>(sm.k1, sm.v1, k_lo + (t + 1) * kBN, k_hi, causal, window, p_min, p_max,
-                         lb, qf, c, st);
+        if (t + 2 < n) {
+            copy_k<D>(L, t + 2, sm.k0);
+            copy_v<D>(L, t + 2, sm.v0);
+        }
+        tile_body<D>(L, t + 1, qf, c, lb, st, sm.k1, sm.v1);
     }
 }
 
-// Q fragments of this lane's row (zeros for rows that do not exist);
-// the sign of a negative scale is folded into Q, which is exact.
+// Q fragments of one row (zeros for rows that do not exist); the sign of a
+// negative scale is folded into Q, which is exact.
 template <int D>
 __device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, bool negate) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
@@ -416,43 +499,42 @@ __device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, bool nega
     }
 }
 
-// Final normalisation and bf16 store of this lane's row: o / l, 0 when l == 0.
+// Final normalisation and bf16 store of one row: o / l, 0 when l == 0.
 template <int D>
-__device__ inline void store_out(const RowState<D>& st, u16* orow, bool valid) {
+__device__ inline void store_out(const f32x16* o, float lpart, u16* orow, bool valid) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    float l = sum_across_halves(st.l);
-    float inv = l > 0.f ? 1.f / l : 0.f;
+    const float l = sum_across_halves(lpart);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     if (!valid) return;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            int d = 32 * dt + 8 * a + 4 * hh;
-            uint2 w = make_uint2(pack_bf16x2(st.o[dt][4 * a] * inv, st.o[dt][4 * a + 1] * inv),
-                                 pack_bf16x2(st.o[dt][4 * a + 2] * inv, st.o[dt][4 * a + 3] * inv));
+            const int d = 32 * dt + 8 * a + 4 * hh;
+            const uint2 w = make_uint2(pack_bf16x2(o[dt][4 * a] * inv, o[dt][4 * a + 1] * inv),
+                                       pack_bf16x2(o[dt][4 * a + 2] * inv, o[dt][4 * a + 3] * inv));
             *reinterpret_cast<uint2*>(orow + d) = w;
         }
 }
 
-// Split partial of this lane's row: unnormalised accumulator, log2-domain
-// maximum (m*c, -inf when nothing was visible) and the sum.
+// Split partial of one row: unnormalised accumulator, log2-domain maximum
+// (m*c, -inf when nothing was visible) and the sum.
 template <int D>
-__device__ inline void store_partial(const RowState<D>& st, float c, float* po, float* pml,
-                                     bool valid) {
+__device__ inline void store_partial(const f32x16* o, float m, float lpart, float c, float* po,
+                                     float* pml, bool valid) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    float l = sum_across_halves(st.l);
+    const float l = sum_across_halves(lpart);
     if (!valid) return;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            int d = 32 * dt + 8 * a + 4 * hh;
+            const int d = 32 * dt + 8 * a + 4 * hh;
             *reinterpret_cast<float4*>(po + d) =
-                make_float4(st.o[dt][4 * a], st.o[dt][4 * a + 1], st.o[dt][4 * a + 2],
-                            st.o[dt][4 * a + 3]);
+                make_float4(o[dt][4 * a], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]);
         }
     if (hh == 0) {
-        pml[0] = st.m == -INFINITY ? -INFINITY : st.m * c;
+        pml[0] = m == -INFINITY ? -INFINITY : m * c;
         pml[1] = l;
     }
 }
@@ -460,9 +542,12 @@ __device__ inline void store_partial(const RowState<D>& st, float c, float* po, 
 template <int D>
 __device__ inline void init_state(RowState<D>& st) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) st.o[dt] = f32x16{};
-    st.m = -INFINITY;
-    st.l = 0.f;
+    for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] = f32x16{};
+        st.m[nt] = -INFINITY;
+        st.l[nt] = 0.f;
+    }
 }
 
 // Key range [lo, hi) of split `split` out of `nsplit` over [lo_all, hi_all).
@@ -527,15 +612,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int r = wave * 32 + (lane & 31);
-    const int hl = r / rm.P, pos = r % rm.P;
-    const int i = q0 + pos;
-    const bool valid = hl < heads_here && i < a.Lq;
-    const int h = hk * g + hc * rm.Gc + hl;
-
     const int64_t p_min = a.q_pos0 + q0;
     const int64_t p_max = a.q_pos0 + min(q0 + rm.P, a.Lq) - 1;
-    const int64_t p_lane = valid ? a.q_pos0 + i : p_max;
+
+    // this lane's row in each of the wave's row tiles
+    int hrow[kNT], irow[kNT];
+    bool valid[kNT];
+    int64_t p_lane[kNT];
+    bf16x8 qf[kNT][D / 16];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int r = (wave * kNT + nt) * 32 + (lane & 31);
+        const int hl = r / rm.P, pos = r % rm.P;
+        irow[nt] = q0 + pos;
+        hrow[nt] = hk * g + hc * rm.Gc + hl;
+        valid[nt] = hl < heads_here && irow[nt] < a.Lq;
+        p_lane[nt] = valid[nt] ? a.q_pos0 + irow[nt] : p_max;
+        load_q<D>(qf[nt],
+                  a.q + b * a.qs[0] + (int64_t)hrow[nt] * a.qs[1] + (int64_t)irow[nt] * a.qs[2],
+                  valid[nt], a.negate);
+    }
 
     // visible keys of the whole workgroup, then this split's share
     int64_t lo64 = a.window > 0 ? p_min - a.window + 1 : 0;
@@ -545,21 +641,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     int k_lo, k_hi;
     split_range((int)lo64, (int)hi64, split, a.nsplit, &k_lo, &k_hi);
 
-    bf16x8 qf[D / 16];
-    load_q<D>(qf, a.q + b * a.qs[0] + (int64_t)h * a.qs[1] + (int64_t)i * a.qs[2], valid,
-              a.negate);
-
     RowState<D> st;
     init_state<D>(st);
     KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
               a.vs[2]};
     attend_range<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
-    if (a.nsplit == 1) {
-        store_out<D>(st, a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2], valid);
-    } else {
-        int64_t row = (((int64_t)split * a.B + b) * a.Hq + h) * a.Lq + i;
-        store_partial<D>(st, a.c, a.part_o + row * D, a.part_ml + row * 2, valid);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        if (a.nsplit == 1) {
+            store_out<D>(st.o[nt], st.l[nt],
+                         a.out + b * a.os[0] + (int64_t)hrow[nt] * a.os[1] +
+                             (int64_t)irow[nt] * a.os[2],
+                         valid[nt]);
+        } else {
+            const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[nt]) * a.Lq + irow[nt];
+            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
+                             a.part_ml + row * 2, valid[nt]);
+        }
     }
 }
 
@@ -715,17 +814,26 @@ __global__ __launch_bounds__(kThreads, 2) void varlen_kernel(VarlenArgs a) {
 
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int r = wave * 32 + (lane & 31);
-    const int hl = r / rm.P, pos = r % rm.P;
-    const int j = qb * rm.P + pos;
-    const bool valid = hl < heads_here && j < sg.q_len;
-    const int h = hk * g + hc * rm.Gc + hl;
-    const int t = sg.q_start + j;
-
     const int64_t base = (int64_t)sg.kv_end - sg.q_len;
     const int64_t p_min = base + qb * rm.P;
     const int64_t p_max = base + min(qb * rm.P + rm.P, sg.q_len) - 1;
-    const int64_t p_lane = valid ? base + j : p_max;
+
+    int hrow[kNT], jrow[kNT];
+    bool valid[kNT];
+    int64_t p_lane[kNT];
+    bf16x8 qf[kNT][D / 16];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int r = (wave * kNT + nt) * 32 + (lane & 31);
+        const int hl = r / rm.P, pos = r % rm.P;
+        jrow[nt] = qb * rm.P + pos;
+        hrow[nt] = hk * g + hc * rm.Gc + hl;
+        valid[nt] = hl < heads_here && jrow[nt] < sg.q_len;
+        p_lane[nt] = valid[nt] ? base + jrow[nt] : p_max;
+        load_q<D>(qf[nt],
+                  a.q + (int64_t)(sg.q_start + jrow[nt]) * a.qs[0] + (int64_t)hrow[nt] * a.qs[1],
+                  valid[nt], a.negate);
+    }
 
     int64_t lo64 = sg.window > 0 ? p_min - sg.window + 1 : 0;
     int64_t hi64 = sg.kv_end;
@@ -735,20 +843,23 @@ __global__ __launch_bounds__(kThreads, 2) void varlen_kernel(VarlenArgs a) {
     int k_lo, k_hi;
     split_range((int)lo64, (int)hi64, split, nsplit, &k_lo, &k_hi);
 
-    bf16x8 qf[D / 16];
-    load_q<D>(qf, a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid, a.negate);
-
     RowState<D> st;
     init_state<D>(st);
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
               a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R};
     attend_range<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
-    if (!splits) {
-        store_out<D>(st, a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1], valid);
-    } else {
-        int64_t row = (((int64_t)seg * qsplit + j) * a.Hq + h) * a.nsplit + split;
-        store_partial<D>(st, a.c, a.part_o + row * D, a.part_ml + row * 2, valid);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int t = sg.q_start + jrow[nt];
+        if (!splits) {
+            store_out<D>(st.o[nt], st.l[nt], a.out + (int64_t)t * a.os[0] + (int64_t)hrow[nt] * a.os[1],
+                         valid[nt]);
+        } else {
+            const int64_t row = (((int64_t)seg * qsplit + jrow[nt]) * a.Hq + hrow[nt]) * a.nsplit + split;
+            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
+                             a.part_ml + row * 2, valid[nt]);
+        }
     }
 }
 
@@ -875,9 +986,10 @@ int check_layout(const char* name, const void* p, const int64_t* str, int n) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Key splits of a prefill launch: enough workgroups to give every compute
-// unit two, with at least 1024 keys per split.
-int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int cus) {
+// Key splits of a prefill launch: enough workgroups to fill every compute
+// unit (two resident at D=128, four at D=64), with at least 1024 keys per
+// split.
+int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
     RowMap rm = row_map(Hq / Hkv);
     int64_t base = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks * B * Hkv;
@@ -887,7 +999,8 @@ int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int cus) {
     if (forced > 0) {
         ns = forced;
     } else {
-        int64_t want = (2 * (int64_t)cus + base - 1) / (base > 0 ? base : 1);
+        const int per_cu = D == 64 ? 4 : 2;
+        int64_t want = (per_cu * (int64_t)cus + base - 1) / (base > 0 ? base : 1);
         ns = (int)(want < kMaxSplits ? want : kMaxSplits);
         if (ns > by_keys) ns = by_keys;
     }
@@ -939,7 +1052,7 @@ size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, in
     if (Lq == 0) return 0;
     DeviceInfo di;
     if (device_info(&di) != ATTN_OK) return 0;
-    return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, di.cus));
+    return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus));
 }
 
 int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, int B, int Hq,
@@ -972,7 +1085,7 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
 
     DeviceInfo di;
     if ((st = device_info(&di))) return st;
-    const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, di.cus);
+    const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus);
     const size_t need = prefill_ws_bytes(B, Hq, Lq, D, nsplit);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -995,7 +1108,9 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     a.Lkv = Lkv;
     a.window = window > 0 ? window : 0;
     a.nsplit = nsplit;
-    a.c = fabsf(scale) * kLog2e;
+    // c > 0 keeps exp2(-inf * c) = 0 for masked scores; a zero scale gives
+    // weights that round to exactly 1 (uniform)
+    a.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
     a.negate = scale < 0.f;
     a.q_pos0 = q_pos0;
     for (int i = 0; i < 4; ++i) {
@@ -1108,7 +1223,9 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.window = window;
     a.ring_rows = ring_rows;
     a.nsplit = nsplit;
-    a.c = fabsf(scale) * kLog2e;
+    // c > 0 keeps exp2(-inf * c) = 0 for masked scores; a zero scale gives
+    // weights that round to exactly 1 (uniform)
+    a.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
     a.negate = scale < 0.f;
     for (int i = 0; i < 3; ++i) {
         a.qs[i] = q_str[i];
