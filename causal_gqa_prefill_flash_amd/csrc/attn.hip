@@ -43,7 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;      // two groups of four: one wave of each group per SIMD
+constexpr int kCopyWaves = 4;  // waves of group 0 issue the K/V tile copies
 constexpr int kThreads = kWave * kWaves;
 constexpr int kNT = 1;                  // 32-row MFMA tiles of query rows per wave
 constexpr int kBM = kWaves * 32 * kNT;  // query rows per workgroup
@@ -138,16 +139,16 @@ struct CopyPlan {
     static constexpr int CH = D / 8;                // 16-byte chunks per row
     static constexpr int ROWS = 64 / CH;            // rows per wave instruction
     static constexpr int INSTR = kBN / ROWS;        // wave instructions per tensor
-    static constexpr int PER_WAVE = INSTR / kWaves;
+    static constexpr int PER_WAVE = INSTR / kCopyWaves;
+    static __device__ int wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
     static __device__ int row(int i) {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-        return (wave + i * kWaves) * ROWS + (threadIdx.x & (kWave - 1)) / CH;
+        return (wave() + i * kCopyWaves) * ROWS + (threadIdx.x & (kWave - 1)) / CH;
     }
     static __device__ int chunk(int i) {
         return ((threadIdx.x & (kWave - 1)) % CH) ^ swz<D>(row(i));
     }
     static __device__ int lds_off(int i) {  // elements
-        return (__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) + i * kWaves) * 512;
+        return (wave() + i * kCopyWaves) * 512;
     }
 };
 
@@ -184,6 +185,14 @@ __device__ inline void issue_rows(const KV& kv, const u16* tb, int64_t rs, int r
 __device__ inline void tile_barrier() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __builtin_amdgcn_s_barrier();
+}
+
+// Workgroup barrier between ping-pong phases; no instruction is scheduled
+// across it, so MFMA and VALU work stay in their phases.
+__device__ inline void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -277,6 +286,15 @@ __device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileSc
             s[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[nt][kk], s[nt][1], 0, 0, 0);
         }
     }
+    // keep 4 fragment reads ahead of the MFMAs: LDS latency hides behind them
+    constexpr int NR = 2 * (D / 16), NM = 2 * kNT * (D / 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (4 + (i + 1) * NR / NM <= NR && (i + 1) * NR % NM == 0)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
 }
 
 // Scores of keys a row does not see become -inf: key k0 + 32t + 8(r/4) +
@@ -365,6 +383,15 @@ __device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st) 
             }
         }
     }
+    // keep 4 fragments (8 transposing reads) ahead of the MFMAs
+    constexpr int NF = (kBN / 16) * (D / 32);  // fragments, 2 reads each
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (f + 4 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
 }
 
 template <int D>
@@ -413,30 +440,81 @@ __device__ inline void copy_v(const KeyLoop<KV>& L, int t, u16* dst) {
     issue_rows<D>(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.k0(t), L.k_hi, dst);
 }
 
-// One key tile (K and V in LDS) for the rows of this wave.  Edge tiles
-// only add an in-place mask of the scores, so every tile runs the same code
-// and the accumulators keep their registers across the loop.
+// Pin the values that cross a phase boundary: an empty asm that reads and
+// rewrites them keeps their producers before it and their consumers after
+// it, so no pass moves MFMA or VALU work into the other phase.
+__device__ inline void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+template <int D>
+__device__ inline void pin_m_outputs(TileScores& S, RowState<D>& st, bool qk, bool pv) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        if (qk) {
+            pin(S[nt][0]);
+            pin(S[nt][1]);
+        }
+        if (pv)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) pin(st.o[nt][dt]);
+    }
+}
+
+template <int D>
+__device__ inline void pin_v_outputs(TileP& pk, RowState<D>& st) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) pin(pk[nt][t][r]);
+        pin(st.m[nt]);
+        pin(st.l[nt]);
+    }
+}
+
+// MFMA phase of a wave: O += P(k-1) V(k-1) (V in Vs) and S(k) = K(k) Q^T (K
+// in Ks).  No VALU work, so the MFMAs issue back to back.
+template <int D, bool QK, bool PV>
+__device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[D / 16],
+                               TileScores& S, const TileP& pk, RowState<D>& st) {
+    if (PV) pv_tile<D>(Vs, pk, st);
+    // separate scheduling regions: keeps the fragment prefetch of the two
+    // products from piling up in registers
+    if (PV && QK) __builtin_amdgcn_sched_barrier(0);
+    if (QK) qk_tile<D>(Ks, qf, S);
+    pin_m_outputs<D>(S, st, QK, PV);
+}
+
+// VALU phase of a wave for tile k: mask (edge tiles), running maxima,
+// rescale of O and l, P(k) and its row sums.
 template <int D, class KV>
-__device__ inline void tile_body(const KeyLoop<KV>& L, int t, const bf16x8 (*qf)[D / 16],
-                                 float c, const LaneBounds* lb, RowState<D>& st, const u16* Ks,
-                                 const u16* Vs) {
-    TileScores S;
-    qk_tile<D>(Ks, qf, S);
-    if (L.needs_mask(t)) mask_tile(S, L.k0(t), lb);
+__device__ inline void v_phase(const KeyLoop<KV>& L, int k, float c, const LaneBounds* lb,
+                               TileScores& S, TileP& pk, RowState<D>& st) {
+    if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
     float alpha[kNT];
     update_max(S, c, st.m, alpha);
     rescale<D>(alpha, st);
-    TileP pk;
     float lsum[kNT];
     softmax_tile(S, c, st.m, pk, lsum);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) st.l[nt] += lsum[nt];
-    pv_tile<D>(Vs, pk, st);
+    pin_v_outputs<D>(pk, st);
 }
 
-// Attend the keys [k_lo, k_hi) for the rows of this wave: tiles alternate
-// between the two LDS stages; the copy of tile t+1 runs while tile t is
-// computed, with one barrier per tile.
+// Attend the keys [k_lo, k_hi) for the rows of this wave.
+//
+// Ping-pong between the two wave groups of the workgroup (one wave of each
+// on every SIMD): every wave alternates an MFMA phase M(k) (the PV product of
+// tile k-1 and the scores of tile k) and a VALU phase (the softmax of tile
+// k), with a workgroup barrier after each phase.  Group 1 starts one phase
+// late, so on every SIMD one wave issues MFMAs while the other runs its
+// softmax.  Group 0 issues the copies of K(k+1) and V(k) at the start of its
+// M(k) (into the stages K(k-1) and V(k-2) vacated) and waits for them at the
+// end of its softmax of tile k; both groups read them from the next phase on.
+// M(0) (scores only) and M(n) (PV only) are peeled off the loop so the loop
+// holds one MFMA phase per LDS stage.
 //   p_lane[nt]: position of this lane's row in row tile nt; p_min/p_max:
 //   extreme positions of the workgroup's rows (for the per-tile mask
 //   decision).
@@ -460,26 +538,64 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     LaneBounds lb[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) lb[nt] = lane_bounds(k_lo, k_hi, causal, window, p_lane[nt]);
+    const bool g0 = CopyPlan<D>::wave() < kCopyWaves;
 
-    copy_k<D>(L, 0, sm.k0);
-    copy_v<D>(L, 0, sm.v0);
-    // unrolled by two so that each stage is a distinct LDS object: the copy
-    // into one stage then never forces a wait before reads of the other
-    for (int t = 0; t < n; t += 2) {
-        tile_barrier();
-        if (t + 1 < n) {
-            copy_k<D>(L, t + 1, sm.k1);
-            copy_v<D>(L, t + 1, sm.v1);
-        }
-        tile_body<D>(L, t, qf, c, lb, st, sm.k0, sm.v0);
-        if (t + 1 >= n) break;
-        tile_barrier();
-        if (t + 2 < n) {
-            copy_k<D>(L, t + 2, sm.k0);
-            copy_v<D>(L, t + 2, sm.v0);
-        }
-        tile_body<D>(L, t + 1, qf, c, lb, st, sm.k1, sm.v1);
+    TileScores S;
+    TileP pk;
+    if (g0) copy_k<D>(L, 0, sm.k0);
+    tile_barrier();
+    if (!g0) phase_barrier();  // group 1 runs one phase behind
+    // M(0): scores of tile 0
+    if (g0) {
+        if (1 < n) copy_k<D>(L, 1, sm.k1);
+        copy_v<D>(L, 0, sm.v0);
     }
+    qk_tile<D>(sm.k0, qf, S);
+    pin_m_outputs<D>(S, st, true, false);
+    phase_barrier();
+    v_phase<D>(L, 0, c, lb, S, pk, st);
+    if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(1), V(0) landed
+    phase_barrier();
+    int k = 1;
+    for (; k + 1 < n; k += 2) {
+        // M(k), k odd: scores of tile k (K in k1), PV of tile k-1 (V in v0)
+        if (g0) {
+            copy_k<D>(L, k + 1, sm.k0);
+            copy_v<D>(L, k, sm.v1);
+        }
+        m_phase<D, true, true>(sm.k1, sm.v0, qf, S, pk, st);
+        phase_barrier();
+        v_phase<D>(L, k, c, lb, S, pk, st);
+        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        phase_barrier();
+        // M(k+1): scores of tile k+1 (K in k0), PV of tile k (V in v1)
+        if (g0) {
+            if (k + 2 < n) copy_k<D>(L, k + 2, sm.k1);
+            copy_v<D>(L, k + 1, sm.v0);
+        }
+        m_phase<D, true, true>(sm.k0, sm.v1, qf, S, pk, st);
+        phase_barrier();
+        v_phase<D>(L, k + 1, c, lb, S, pk, st);
+        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        phase_barrier();
+    }
+    if (k < n) {
+        // M(n-1), n-1 odd: scores of tile n-1 (K in k1), PV of tile n-2 (V in v0)
+        if (g0) copy_v<D>(L, k, sm.v1);
+        m_phase<D, true, true>(sm.k1, sm.v0, qf, S, pk, st);
+        phase_barrier();
+        v_phase<D>(L, k, c, lb, S, pk, st);
+        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        phase_barrier();
+        ++k;
+    }
+    // M(n): PV of tile n-1, whose V sits in stage (n-1) % 2
+    if ((n - 1) & 1)
+        pv_tile<D>(sm.v1, pk, st);
+    else
+        pv_tile<D>(sm.v0, pk, st);
+    phase_barrier();
+    if (g0) phase_barrier();  // matches group 1's extra barrier
 }
 
 // Q fragments of one row (zeros for rows that do not exist); the sign of a
@@ -597,7 +713,7 @@ __device__ inline int xcd_remap(int L, int N) {
     const TileSmem<D> sm{sk0, sv0, sk1, sv1}
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     DECLARE_TILE_SMEM(D);
 
     const int g = a.Hq / a.Hkv;
@@ -782,7 +898,7 @@ __device__ inline bool seg_splits(const Segment& g, int qsplit, int nsplit) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void varlen_kernel(VarlenArgs a) {
+__global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     DECLARE_TILE_SMEM(D);
 
     const int g = a.Hq / a.Hkv;
@@ -987,7 +1103,7 @@ int check_layout(const char* name, const void* p, const int64_t* str, int n) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Key splits of a prefill launch: enough workgroups to fill every compute
-// unit (two resident at D=128, four at D=64), with at least 1024 keys per
+// unit (one resident at D=128, two at D=64), with at least 1024 keys per
 // split.
 int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
@@ -999,7 +1115,7 @@ int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
     if (forced > 0) {
         ns = forced;
     } else {
-        const int per_cu = D == 64 ? 4 : 2;
+        const int per_cu = D == 64 ? 2 : 1;
         int64_t want = (per_cu * (int64_t)cus + base - 1) / (base > 0 ? base : 1);
         ns = (int)(want < kMaxSplits ? want : kMaxSplits);
         if (ns > by_keys) ns = by_keys;
