@@ -152,23 +152,44 @@ struct CopyPlan {
     }
 };
 
+// Per-lane byte offsets of this wave's copy instructions inside a tile of
+// consecutive rows (row * stride + chunk), the same for every tile.
+template <int D>
+struct CopyOffsets {
+    uint32_t o[CopyPlan<D>::PER_WAVE];
+};
+
+template <int D>
+__device__ inline CopyOffsets<D> copy_offsets(int rs2) {
+    CopyOffsets<D> c;
+#pragma unroll
+    for (int i = 0; i < CopyPlan<D>::PER_WAVE; ++i)
+        c.o[i] = (uint32_t)(CopyPlan<D>::row(i) * rs2 + 16 * CopyPlan<D>::chunk(i));
+    return c;
+}
+
 // Enqueue global -> LDS copies of the rows of keys [k0, k0 + kBN) of one
-// tensor (K or V); keys at or past k_hi re-read the last key of the range
-// (their scores are masked).  rs2: row stride in bytes when a tile's rows
-// span less than 2^31 bytes (else 0: the per-row path is taken).
+// tensor (K or V).  Tiles of consecutive rows go through a buffer resource
+// that spans exactly the rows below k_hi: rows past it read as zeros and
+// touch no memory.  A tile that wraps a ring takes the per-row path.
+// rs2: row stride in bytes when a tile's rows span less than 2^31 bytes,
+// else 0 (per-row path).
 template <int D, class KV>
-__device__ inline void issue_rows(const KV& kv, const u16* tb, int64_t rs, int rs2, int k0,
-                                  int k_hi, u16* dst) {
+__device__ inline void issue_rows(const KV& kv, const u16* tb, int64_t rs, int rs2,
+                                  const CopyOffsets<D>& co, int k0, int k_hi, u16* dst) {
     typedef CopyPlan<D> CP;
     const int base = kv.row(k0);
-    if (rs2 > 0 && k0 + kBN <= k_hi && kv.contiguous(k0, kBN)) {
-        // full tile of consecutive rows: scalar tile base + 32-bit lane offset
-        const char* t = reinterpret_cast<const char*>(tb + (int64_t)base * rs);
+    const int nvalid = k_hi - k0 < kBN ? k_hi - k0 : kBN;
+    if (rs2 > 0 && kv.contiguous(k0, nvalid)) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
+        const uint32_t nrec = (uint32_t)((nvalid - 1) * rs2 + 2 * D);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(tb + (int64_t)base * rs), 0, nrec, 0x00020000);
 #pragma unroll
         for (int i = 0; i < CP::PER_WAVE; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (glb_void*)(t + (uint32_t)(CP::row(i) * rs2 + 16 * CP::chunk(i))),
-                (lds_void*)(dst + CP::lds_off(i)), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + CP::lds_off(i)), 16,
+                                                     co.o[i], 0, 0, 0);
+#endif
     } else {
 #pragma unroll
         for (int i = 0; i < CP::PER_WAVE; ++i) {
@@ -321,11 +342,13 @@ __device__ inline void mask_tile(TileScores& s, int k0, const LaneBounds* lb) {
 __device__ inline void update_max(const TileScores& s, float c, float* m, float* alpha) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        float mx = m[nt];
+        float mq[4] = {m[nt], -INFINITY, -INFINITY, -INFINITY};  // 4 independent chains
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[nt][t][r]);
+            for (int r = 0; r < 16; ++r) mq[r & 3] = __builtin_fmaxf(mq[r & 3], s[nt][t][r]);
+        const float mx =
+            __builtin_fmaxf(__builtin_fmaxf(mq[0], mq[1]), __builtin_fmaxf(mq[2], mq[3]));
         const float m_new = max_across_halves(mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;  // guard: nothing visible yet
         alpha[nt] = m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[nt] - m_use) * c);
@@ -344,7 +367,7 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const float mc = (m[nt] == -INFINITY ? 0.f : m[nt]) * c;
-        float ls0 = 0.f, ls1 = 0.f;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -353,14 +376,10 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
                 const float x1 = __builtin_amdgcn_exp2f(fmaf(s[nt][t][r + 1], c, -mc));
                 const uint32_t w = pack_bf16x2(x0, x1);
                 pk[nt][t][r >> 1] = w;
-                if (r & 2)
-                    ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
-                                                          ls1, false);
-                else
-                    ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones,
-                                                          ls0, false);
+                ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                                                   ones, ls[(r >> 1) & 3], false);
             }
-        lsum[nt] = ls0 + ls1;
+        lsum[nt] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
 }
 
@@ -416,28 +435,51 @@ struct TileSmem {
 };
 
 // Per-range constants of the key loop.
-template <class KV>
+template <int D, class KV>
 struct KeyLoop {
     KV kv;
-    int k_lo, k_hi, causal, window;
-    int64_t p_min, p_max;
-    int ks2, vs2;  // byte strides for the full-tile copy path (0: per-row path)
+    int k_lo, k_hi;
+    int ks2, vs2;              // byte strides for the buffer copy path (0: per-row path)
+    CopyOffsets<D> kco, vco;   // per-lane copy offsets (full tiles)
+    int t_in0, t_in1;          // tiles t_in0 <= t < t_in1 need no mask
     __device__ int k0(int t) const { return k_lo + t * kBN; }
     // a tile straddles a causal, window or range edge of some row
-    __device__ bool needs_mask(int t) const {
-        const int a = k0(t);
-        return (a + kBN > k_hi) || (causal && (int64_t)a + kBN - 1 > p_min) ||
-               (window > 0 && (int64_t)a <= p_max - window);
-    }
+    __device__ bool needs_mask(int t) const { return t < t_in0 || t >= t_in1; }
 };
 
+// Tiles of [k_lo, k_hi) that need no mask: every key of the tile lies below
+// k_hi, at or before the smallest row position (causal) and past the window
+// start of the largest.
 template <int D, class KV>
-__device__ inline void copy_k(const KeyLoop<KV>& L, int t, u16* dst) {
-    issue_rows<D>(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.k0(t), L.k_hi, dst);
+__device__ inline void interior_tiles(KeyLoop<D, KV>& L, int causal, int window, int64_t p_min,
+                                      int64_t p_max) {
+    const int n = (L.k_hi - L.k_lo + kBN - 1) / kBN;
+    int64_t t1 = (L.k_hi - L.k_lo) / kBN;  // full tiles
+    if (causal) {
+        // k_lo + t*kBN + kBN - 1 <= p_min
+        const int64_t c = p_min - L.k_lo - (kBN - 1);
+        const int64_t tc = c < 0 ? 0 : c / kBN + 1;
+        if (tc < t1) t1 = tc;
+    }
+    int64_t t0 = 0;
+    if (window > 0) {
+        // k_lo + t*kBN > p_max - window
+        const int64_t w = p_max - window - L.k_lo;
+        t0 = w < 0 ? 0 : w / kBN + 1;
+    }
+    if (t1 > n) t1 = n;
+    if (t0 > t1) t0 = t1;
+    L.t_in0 = (int)t0;
+    L.t_in1 = (int)t1;
+}
+
+template <int D, class KV>
+__device__ inline void copy_k(const KeyLoop<D, KV>& L, int t, u16* dst) {
+    issue_rows<D>(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.kco, L.k0(t), L.k_hi, dst);
 }
 template <int D, class KV>
-__device__ inline void copy_v(const KeyLoop<KV>& L, int t, u16* dst) {
-    issue_rows<D>(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.k0(t), L.k_hi, dst);
+__device__ inline void copy_v(const KeyLoop<D, KV>& L, int t, u16* dst) {
+    issue_rows<D>(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.vco, L.k0(t), L.k_hi, dst);
 }
 
 // Pin the values that cross a phase boundary: an empty asm that reads and
@@ -490,7 +532,7 @@ __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[
 // VALU phase of a wave for tile k: mask (edge tiles), running maxima,
 // rescale of O and l, P(k) and its row sums.
 template <int D, class KV>
-__device__ inline void v_phase(const KeyLoop<KV>& L, int k, float c, const LaneBounds* lb,
+__device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const LaneBounds* lb,
                                TileScores& S, TileP& pk, RowState<D>& st) {
     if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
     float alpha[kNT];
@@ -524,16 +566,15 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
                              const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
                              const TileSmem<D>& sm) {
     if (k_lo >= k_hi) return;
-    KeyLoop<KV> L;
+    KeyLoop<D, KV> L;
     L.kv = kv;
     L.k_lo = k_lo;
     L.k_hi = k_hi;
-    L.causal = causal;
-    L.window = window;
-    L.p_min = p_min;
-    L.p_max = p_max;
     L.ks2 = kv.ks * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.ks * 2) : 0;
     L.vs2 = kv.vs * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.vs * 2) : 0;
+    L.kco = copy_offsets<D>(L.ks2);
+    L.vco = copy_offsets<D>(L.vs2);
+    interior_tiles<D>(L, causal, window, p_min, p_max);
     const int n = (k_hi - k_lo + kBN - 1) / kBN;
     LaneBounds lb[kNT];
 #pragma unroll
