@@ -44,7 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;      // two groups of four: one wave of each group per SIMD
-constexpr int kCopyWaves = 4;  // waves of group 0 issue the K/V tile copies
+constexpr int kCopyWaves = 8;  // waves that issue the K/V tile copies
 constexpr int kThreads = kWave * kWaves;
 constexpr int kNT = 1;                  // 32-row MFMA tiles of query rows per wave
 constexpr int kBM = kWaves * 32 * kNT;  // query rows per workgroup
@@ -168,38 +168,96 @@ __device__ inline CopyOffsets<D> copy_offsets(int rs2) {
     return c;
 }
 
-// Enqueue global -> LDS copies of the rows of keys [k0, k0 + kBN) of one
-// tensor (K or V).  Tiles of consecutive rows go through a buffer resource
-// that spans exactly the rows below k_hi: rows past it read as zeros and
-// touch no memory.  A tile that wraps a ring takes the per-row path.
-// rs2: row stride in bytes when a tile's rows span less than 2^31 bytes,
-// else 0 (per-row path).
-template <int D, class KV>
-__device__ inline void issue_rows(const KV& kv, const u16* tb, int64_t rs, int rs2,
-                                  const CopyOffsets<D>& co, int k0, int k_hi, u16* dst) {
-    typedef CopyPlan<D> CP;
-    const int base = kv.row(k0);
-    const int nvalid = k_hi - k0 < kBN ? k_hi - k0 : kBN;
-    if (rs2 > 0 && kv.contiguous(k0, nvalid)) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-        const uint32_t nrec = (uint32_t)((nvalid - 1) * rs2 + 2 * D);
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(tb + (int64_t)base * rs), 0, nrec, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < CP::PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + CP::lds_off(i)), 16,
-                                                     co.o[i], 0, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+#else
+struct BufRsrc {  // placeholder: buffer resources exist only in the device pass
+    int w[4];
+};
 #endif
-    } else {
-#pragma unroll
-        for (int i = 0; i < CP::PER_WAVE; ++i) {
-            const int r = CP::row(i);
-            const int off = k0 + r < k_hi ? r : k_hi - 1 - k0;
-            const int row = kv.advance(base, off);
-            __builtin_amdgcn_global_load_lds((glb_void*)(tb + (int64_t)row * rs + 8 * CP::chunk(i)),
-                                             (lds_void*)(dst + CP::lds_off(i)), 16, 0, 0);
-        }
+
+// This wave's share of the global -> LDS copy of keys [k0, k0 + kBN) of one
+// tensor (K or V) of flat storage, prepared with scalar work and issued one
+// instruction at a time, without branches, so that the instructions can sit
+// between MFMAs.  The copy goes through a buffer resource spanning exactly
+// the rows below k_hi: rows past it, and every row of a tile at or past
+// k_hi (whose stage nobody reads), land in LDS as zeros and touch no memory.
+template <int D>
+struct TileCopyFlat {
+    static constexpr int N = CopyPlan<D>::PER_WAVE;
+    BufRsrc r;
+    u16* dst;
+    const uint32_t* o;
+    __device__ TileCopyFlat(const KVFlat&, const u16* tb, int64_t rs, int rs2,
+                            const CopyOffsets<D>& co, int64_t k0, int k_hi, u16* d)
+        : dst(d), o(co.o) {
+        const int64_t nl = k_hi - k0;
+        const int nv = nl < 0 ? 0 : (nl > kBN ? kBN : (int)nl);
+        const uint32_t nrec = nv > 0 ? (uint32_t)((nv - 1) * rs2 + 2 * D) : 0u;
+#if defined(__HIP_DEVICE_COMPILE__)
+        r = __builtin_amdgcn_make_buffer_rsrc((void*)(tb + (nv > 0 ? k0 : 0) * rs), 0,
+                                              nrec, 0x00020000);
+#else
+        (void)tb, (void)rs, (void)nrec;
+#endif
     }
+    __device__ void issue(int i) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + CopyPlan<D>::lds_off(i)), 16,
+                                                 o[i], 0, 0, 0);
+#else
+        (void)i;
+#endif
+    }
+};
+
+// The same for one column of ring storage: each lane addresses its own row
+// (position mod R), so a tile may wrap the ring.  Rows past k_hi repeat row
+// k_hi - 1, and a tile at or past k_hi copies row k_hi - 1 throughout.
+template <int D>
+struct TileCopyRing {
+    static constexpr int N = CopyPlan<D>::PER_WAVE;
+    const u16* tb;
+    int64_t rs;
+    int R, kc, last;
+    u16* dst;
+    __device__ TileCopyRing(const KVRing& kv, const u16* t, int64_t s, int, const CopyOffsets<D>&,
+                            int64_t k0, int k_hi, u16* d)
+        : tb(t), rs(s), R(kv.R), dst(d) {
+        kc = k0 < k_hi ? (int)k0 : k_hi - 1;
+        last = k_hi - 1 - kc;
+    }
+    __device__ void issue(int i) const {
+        const int r = CopyPlan<D>::row(i);
+        const unsigned pos = (unsigned)(kc + (r < last ? r : last));
+        const unsigned row = pos % (unsigned)R;
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(tb + (int64_t)row * rs + 8 * CopyPlan<D>::chunk(i)),
+            (lds_void*)(dst + CopyPlan<D>::lds_off(i)), 16, 0, 0);
+    }
+};
+
+template <int D, class KV>
+struct TileCopySel;
+template <int D>
+struct TileCopySel<D, KVFlat> {
+    typedef TileCopyFlat<D> T;
+};
+template <int D>
+struct TileCopySel<D, KVRing> {
+    typedef TileCopyRing<D> T;
+};
+
+// No copy (an MFMA region without copies).
+struct NoCopy {
+    static constexpr int N = 0;
+    __device__ void issue(int) const {}
+};
+
+// Positions of the copy instructions among the NM MFMAs of a region: copy j
+// of NC follows MFMA slot(j), spread evenly.
+__device__ __host__ constexpr int copy_slot(int j, int NC, int NM) {
+    return j * NM / NC + NM / (2 * NC);
 }
 
 // Wait for this wave's outstanding global -> LDS copies, then for every wave.
@@ -292,10 +350,13 @@ __device__ inline LaneBounds lane_bounds(int k_lo, int k_hi, int causal, int win
 typedef f32x16 TileScores[kNT][2];
 
 // S^T = K Q^T for one key tile (keys in LDS).  Each K fragment read from LDS
-// feeds the MFMAs of all kNT row tiles.
-template <int D>
-__device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileScores& s) {
+// feeds the MFMAs of all kNT row tiles.  The copy instructions of c1 and c2
+// are spread between the MFMAs.
+template <int D, class C1, class C2>
+__device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileScores& s,
+                               const C1& c1, const C2& c2) {
     const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NR = 2 * (D / 16), NM = 2 * kNT * (D / 16), NC = C1::N + C2::N;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) s[nt][0] = s[nt][1] = f32x16{};
 #pragma unroll
@@ -306,15 +367,27 @@ __device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileSc
             s[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[nt][kk], s[nt][0], 0, 0, 0);
             s[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[nt][kk], s[nt][1], 0, 0, 0);
         }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int sl = copy_slot(j, NC, NM);
+            if (sl >= 2 * kNT * kk && sl < 2 * kNT * (kk + 1)) {
+                if (j < C1::N)
+                    c1.issue(j);
+                else
+                    c2.issue(j - C1::N);
+            }
+        }
     }
     // keep 4 fragment reads ahead of the MFMAs: LDS latency hides behind them
-    constexpr int NR = 2 * (D / 16), NM = 2 * kNT * (D / 16);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (4 + (i + 1) * NR / NM <= NR && (i + 1) * NR % NM == 0)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            if (copy_slot(j, NC, NM) == i) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
 }
 
@@ -366,7 +439,7 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        const float mc = (m[nt] == -INFINITY ? 0.f : m[nt]) * c;
+        const float mc = (m[nt] == -INFINITY ? 0.f : m[nt]) * c;  // reference 0 before any key
         float ls[4] = {0.f, 0.f, 0.f, 0.f};  // 4 independent chains
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -384,10 +457,13 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
 }
 
 // O^T += V^T P^T for one key tile (V in LDS), 16 keys per MFMA; each V
-// fragment feeds the MFMAs of all kNT row tiles.
-template <int D>
-__device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st) {
+// fragment feeds the MFMAs of all kNT row tiles.  The copy instructions of
+// c1 are spread between the MFMAs.
+template <int D, class C1>
+__device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st, const C1& c1) {
     const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NF = (kBN / 16) * (D / 32);  // fragments, 2 reads each
+    constexpr int NC = C1::N;
 #pragma unroll
     for (int c4 = 0; c4 < kBN / 16; ++c4) {
 #pragma unroll
@@ -400,16 +476,22 @@ __device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st) 
                 st.o[nt][dt] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[nt][dt], 0, 0, 0);
             }
+            const int f = c4 * (D / 32) + dt;
+#pragma unroll
+            for (int j = 0; j < NC; ++j)
+                if (copy_slot(j, NC, NF) == f) c1.issue(j);
         }
     }
     // keep 4 fragments (8 transposing reads) ahead of the MFMAs
-    constexpr int NF = (kBN / 16) * (D / 32);  // fragments, 2 reads each
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (f + 4 < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            if (copy_slot(j, NC, NF) == f) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
 }
 
@@ -425,13 +507,12 @@ __device__ inline void rescale(const float* alpha, RowState<D>& st) {
     }
 }
 
-// LDS of one workgroup: two stages of K and V tiles.
+// LDS of one workgroup: three stages of K and V tiles.
 template <int D>
 struct TileSmem {
-    u16* k0;
-    u16* v0;
-    u16* k1;
-    u16* v1;
+    u16* k[3];
+    u16* v[3];
+    int* rerun;  // set when the fixed-reference pass must be redone exactly
 };
 
 // Per-range constants of the key loop.
@@ -439,10 +520,11 @@ template <int D, class KV>
 struct KeyLoop {
     KV kv;
     int k_lo, k_hi;
-    int ks2, vs2;              // byte strides for the buffer copy path (0: per-row path)
+    int ks2, vs2;              // row strides in bytes (flat storage: below 2^25)
     CopyOffsets<D> kco, vco;   // per-lane copy offsets (full tiles)
     int t_in0, t_in1;          // tiles t_in0 <= t < t_in1 need no mask
     __device__ int k0(int t) const { return k_lo + t * kBN; }
+    __device__ int64_t k0l(int t) const { return (int64_t)k_lo + (int64_t)t * kBN; }
     // a tile straddles a causal, window or range edge of some row
     __device__ bool needs_mask(int t) const { return t < t_in0 || t >= t_in1; }
 };
@@ -471,15 +553,6 @@ __device__ inline void interior_tiles(KeyLoop<D, KV>& L, int causal, int window,
     if (t0 > t1) t0 = t1;
     L.t_in0 = (int)t0;
     L.t_in1 = (int)t1;
-}
-
-template <int D, class KV>
-__device__ inline void copy_k(const KeyLoop<D, KV>& L, int t, u16* dst) {
-    issue_rows<D>(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.kco, L.k0(t), L.k_hi, dst);
-}
-template <int D, class KV>
-__device__ inline void copy_v(const KeyLoop<D, KV>& L, int t, u16* dst) {
-    issue_rows<D>(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.vco, L.k0(t), L.k_hi, dst);
 }
 
 // Pin the values that cross a phase boundary: an empty asm that reads and
@@ -517,27 +590,35 @@ __device__ inline void pin_v_outputs(TileP& pk, RowState<D>& st) {
 }
 
 // MFMA phase of a wave: O += P(k-1) V(k-1) (V in Vs) and S(k) = K(k) Q^T (K
-// in Ks).  No VALU work, so the MFMAs issue back to back.
-template <int D, bool QK, bool PV>
+// in Ks), with this wave's copies of a later K tile (ck) spread through the
+// PV product and of a later V tile (cv) through the scores.  No VALU work,
+// so the MFMAs issue back to back.
+template <int D, bool QK, bool PV, class CK, class CV>
 __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[D / 16],
-                               TileScores& S, const TileP& pk, RowState<D>& st) {
-    if (PV) pv_tile<D>(Vs, pk, st);
+                               TileScores& S, const TileP& pk, RowState<D>& st, const CK& ck,
+                               const CV& cv) {
+    if (PV) pv_tile<D>(Vs, pk, st, ck);
     // separate scheduling regions: keeps the fragment prefetch of the two
     // products from piling up in registers
     if (PV && QK) __builtin_amdgcn_sched_barrier(0);
-    if (QK) qk_tile<D>(Ks, qf, S);
+    if (QK) qk_tile<D>(Ks, qf, S, cv, NoCopy{});
     pin_m_outputs<D>(S, st, QK, PV);
 }
 
-// VALU phase of a wave for tile k: mask (edge tiles), running maxima,
-// rescale of O and l, P(k) and its row sums.
-template <int D, class KV>
+// VALU phase of a wave for tile k: mask (edge tiles), then P(k) and its row
+// sums.  EXACT: against each row's running maximum, with the rescale of O
+// and l when it moves.  Otherwise against the row's fixed reference st.m (0
+// while it is -inf), with no maxima and no rescale; the caller checks
+// afterwards that every row's sum stayed in range.
+template <int D, bool EXACT, class KV>
 __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const LaneBounds* lb,
                                TileScores& S, TileP& pk, RowState<D>& st) {
     if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
-    float alpha[kNT];
-    update_max(S, c, st.m, alpha);
-    rescale<D>(alpha, st);
+    if (EXACT) {
+        float alpha[kNT];
+        update_max(S, c, st.m, alpha);
+        rescale<D>(alpha, st);
+    }
     float lsum[kNT];
     softmax_tile(S, c, st.m, pk, lsum);
 #pragma unroll
@@ -545,33 +626,77 @@ __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const La
     pin_v_outputs<D>(pk, st);
 }
 
+// End of an MFMA phase: wait until at most NPEND of this wave's copies are
+// in flight (those issued in this phase), then the workgroup barrier.
+template <int NPEND>
+__device__ inline void copy_wait_barrier() {
+    static_assert(NPEND >= 0 && NPEND < 16, "vmcnt field");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NPEND);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, class KV>
+__device__ inline typename TileCopySel<D, KV>::T k_copy(const KeyLoop<D, KV>& L, int t, u16* dst) {
+    return typename TileCopySel<D, KV>::T(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.kco, L.k0l(t), L.k_hi,
+                                          dst);
+}
+template <int D, class KV>
+__device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L, int t, u16* dst) {
+    return typename TileCopySel<D, KV>::T(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.vco, L.k0l(t), L.k_hi,
+                                          dst);
+}
+
+// One ping-pong step for tile k >= 1: the MFMA phase M(k) (scores of tile k
+// from Kr, PV of tile k-1 from Vr) with the copies of K(k+2) into Kw and
+// V(k+1) into Vw, then the softmax phase of tile k, each closed by a
+// workgroup barrier.  At the end of M(k) every wave waits for its copies of
+// the previous step (K(k+1), V(k)); those of this step stay in flight.
+template <int D, bool EXACT, class KV>
+__device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
+                               float c, const LaneBounds* lb, TileScores& S, TileP& pk,
+                               RowState<D>& st, const u16* Kr, const u16* Vr, u16* Kw, u16* Vw) {
+    typedef typename TileCopySel<D, KV>::T TC;
+    const TC ck = k_copy<D>(L, k + 2, Kw);
+    const TC cv = v_copy<D>(L, k + 1, Vw);
+    m_phase<D, true, true>(Kr, Vr, qf, S, pk, st, ck, cv);
+    copy_wait_barrier<2 * TC::N>();
+    v_phase<D, EXACT>(L, k, c, lb, S, pk, st);
+    phase_barrier();
+}
+
 // Attend the keys [k_lo, k_hi) for the rows of this wave.
 //
-// Ping-pong between the two wave groups of the workgroup (one wave of each
-// on every SIMD): every wave alternates an MFMA phase M(k) (the PV product of
-// tile k-1 and the scores of tile k) and a VALU phase (the softmax of tile
-// k), with a workgroup barrier after each phase.  Group 1 starts one phase
-// late, so on every SIMD one wave issues MFMAs while the other runs its
-// softmax.  Group 0 issues the copies of K(k+1) and V(k) at the start of its
-// M(k) (into the stages K(k-1) and V(k-2) vacated) and waits for them at the
-// end of its softmax of tile k; both groups read them from the next phase on.
-// M(0) (scores only) and M(n) (PV only) are peeled off the loop so the loop
-// holds one MFMA phase per LDS stage.
+// Ping-pong between the two wave groups of the workgroup (waves 0-3 and
+// 4-7, one of each on every SIMD): every wave alternates an MFMA phase M(k)
+// (the PV product of tile k-1 and the scores of tile k) and a VALU phase
+// (the softmax of tile k), with a workgroup barrier after each phase.  Group
+// 1 starts one phase late, so on every SIMD one wave issues MFMAs while the
+// other runs its softmax.  K and V tiles stream through three LDS stages
+// each: during M(k) every wave issues its share of the copies of K(k+2) and
+// V(k+1) (into the stages of K(k-1) and V(k-2), which both groups have
+// finished reading), spread between its MFMAs, and at the end of M(k) waits
+// for its share of K(k+1) and V(k), which the next MFMA phases read.
+// Copies of tiles past the range fill unread stages.  M(0) (scores only) and
+// M(n) (PV only) are peeled off the loop, which is unrolled by three so that
+// every stage is a distinct LDS object.
 //   p_lane[nt]: position of this lane's row in row tile nt; p_min/p_max:
 //   extreme positions of the workgroup's rows (for the per-tile mask
 //   decision).
-template <int D, class KV>
+template <int D, bool EXACT, class KV>
 __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
                              const int64_t* p_lane, int64_t p_min, int64_t p_max,
                              const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
                              const TileSmem<D>& sm) {
     if (k_lo >= k_hi) return;
+    typedef typename TileCopySel<D, KV>::T TC;
     KeyLoop<D, KV> L;
     L.kv = kv;
     L.k_lo = k_lo;
     L.k_hi = k_hi;
-    L.ks2 = kv.ks * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.ks * 2) : 0;
-    L.vs2 = kv.vs * 2 * kBN < (int64_t)1 << 31 ? (int)(kv.vs * 2) : 0;
+    L.ks2 = (int)(kv.ks * 2);  // below 2^25 (host check) for flat storage
+    L.vs2 = (int)(kv.vs * 2);
     L.kco = copy_offsets<D>(L.ks2);
     L.vco = copy_offsets<D>(L.vs2);
     interior_tiles<D>(L, causal, window, p_min, p_max);
@@ -579,64 +704,57 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     LaneBounds lb[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) lb[nt] = lane_bounds(k_lo, k_hi, causal, window, p_lane[nt]);
-    const bool g0 = CopyPlan<D>::wave() < kCopyWaves;
+    const bool g1 = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) >= kWaves / 2;
 
     TileScores S;
     TileP pk;
-    if (g0) copy_k<D>(L, 0, sm.k0);
-    tile_barrier();
-    if (!g0) phase_barrier();  // group 1 runs one phase behind
-    // M(0): scores of tile 0
-    if (g0) {
-        if (1 < n) copy_k<D>(L, 1, sm.k1);
-        copy_v<D>(L, 0, sm.v0);
+    {
+        const TC k0c = k_copy<D>(L, 0, sm.k[0]), k1c = k_copy<D>(L, 1, sm.k[1]);
+        const TC v0c = v_copy<D>(L, 0, sm.v[0]);
+#pragma unroll
+        for (int i = 0; i < TC::N; ++i) {
+            k0c.issue(i);
+            k1c.issue(i);
+            v0c.issue(i);
+        }
     }
-    qk_tile<D>(sm.k0, qf, S);
-    pin_m_outputs<D>(S, st, true, false);
-    phase_barrier();
-    v_phase<D>(L, 0, c, lb, S, pk, st);
-    if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(1), V(0) landed
+    tile_barrier();
+    if (g1) phase_barrier();  // group 1 runs one phase behind
+    {
+        // M(0): scores of tile 0, copies of K(2) and V(1)
+        const TC ck = k_copy<D>(L, 2, sm.k[2]), cv = v_copy<D>(L, 1, sm.v[1]);
+        qk_tile<D>(sm.k[0], qf, S, ck, cv);
+        pin_m_outputs<D>(S, st, true, false);
+        copy_wait_barrier<2 * TC::N>();
+    }
+    v_phase<D, true>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
     phase_barrier();
     int k = 1;
-    for (; k + 1 < n; k += 2) {
-        // M(k), k odd: scores of tile k (K in k1), PV of tile k-1 (V in v0)
-        if (g0) {
-            copy_k<D>(L, k + 1, sm.k0);
-            copy_v<D>(L, k, sm.v1);
-        }
-        m_phase<D, true, true>(sm.k1, sm.v0, qf, S, pk, st);
-        phase_barrier();
-        v_phase<D>(L, k, c, lb, S, pk, st);
-        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
-        phase_barrier();
-        // M(k+1): scores of tile k+1 (K in k0), PV of tile k (V in v1)
-        if (g0) {
-            if (k + 2 < n) copy_k<D>(L, k + 2, sm.k1);
-            copy_v<D>(L, k + 1, sm.v0);
-        }
-        m_phase<D, true, true>(sm.k0, sm.v1, qf, S, pk, st);
-        phase_barrier();
-        v_phase<D>(L, k + 1, c, lb, S, pk, st);
-        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
-        phase_barrier();
+    for (; k + 2 < n; k += 3) {
+        // k = 1 mod 3: K(k) in stage 1, V(k-1) in stage 0; write K(k+2) -> 0, V(k+1) -> 2
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], sm.k[0], sm.v[2]);
+        pp_step<D, EXACT>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], sm.k[1], sm.v[0]);
+        pp_step<D, EXACT>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], sm.k[2], sm.v[1]);
     }
     if (k < n) {
-        // M(n-1), n-1 odd: scores of tile n-1 (K in k1), PV of tile n-2 (V in v0)
-        if (g0) copy_v<D>(L, k, sm.v1);
-        m_phase<D, true, true>(sm.k1, sm.v0, qf, S, pk, st);
-        phase_barrier();
-        v_phase<D>(L, k, c, lb, S, pk, st);
-        if (g0) __builtin_amdgcn_s_waitcnt(0x0F70);
-        phase_barrier();
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], sm.k[0], sm.v[2]);
         ++k;
     }
-    // M(n): PV of tile n-1, whose V sits in stage (n-1) % 2
-    if ((n - 1) & 1)
-        pv_tile<D>(sm.v1, pk, st);
+    if (k < n) {
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], sm.k[1], sm.v[0]);
+        ++k;
+    }
+    // M(n): PV of tile n-1, whose V sits in stage (n-1) % 3; then no copy
+    // is left in flight
+    const int sv = (n - 1) % 3;
+    if (sv == 0)
+        pv_tile<D>(sm.v[0], pk, st, NoCopy{});
+    else if (sv == 1)
+        pv_tile<D>(sm.v[1], pk, st, NoCopy{});
     else
-        pv_tile<D>(sm.v0, pk, st);
-    phase_barrier();
-    if (g0) phase_barrier();  // matches group 1's extra barrier
+        pv_tile<D>(sm.v[2], pk, st, NoCopy{});
+    copy_wait_barrier<0>();
+    if (!g1) phase_barrier();  // matches group 1's extra barrier
 }
 
 // Q fragments of one row (zeros for rows that do not exist); the sign of a
@@ -691,7 +809,7 @@ __device__ inline void store_partial(const f32x16* o, float m, float lpart, floa
                 make_float4(o[dt][4 * a], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]);
         }
     if (hh == 0) {
-        pml[0] = m == -INFINITY ? -INFINITY : m * c;
+        pml[0] = l > 0.f ? (m == -INFINITY ? 0.f : m * c) : -INFINITY;
         pml[1] = l;
     }
 }
@@ -716,6 +834,37 @@ __device__ inline void split_range(int lo_all, int hi_all, int split, int nsplit
     int b = a + chunk;
     *lo = a < hi_all ? a : hi_all;
     *hi = b < hi_all ? b : hi_all;
+}
+
+// Attend the keys [k_lo, k_hi) for the rows of the workgroup.  The first
+// pass takes the exact maximum of the first tile as each row's reference
+// and keeps it: later tiles need neither maxima nor rescales (softmax does
+// not depend on the reference).  That is exact as long as no P overflows
+// and the sum of a row that sees keys does not underflow, so every row
+// checks that its sum lies in [2^-64, 2^64] (which bounds each P of the
+// row); if any row of the workgroup fails, the workgroup redoes the range
+// with the exact running-maximum pass.
+template <int D, class KV>
+__device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
+                       const int64_t* p_lane, int64_t p_min, int64_t p_max,
+                       const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
+                       const TileSmem<D>& sm) {
+    if (threadIdx.x == 0) *sm.rerun = 0;
+    attend_range<D, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st, sm);
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float l = sum_across_halves(st.l[nt]);
+        const bool sees = lane_bounds(k_lo, k_hi, causal, window, p_lane[nt]).lo < k_hi;
+        bad |= sees && !(l >= 0x1p-64f && l <= 0x1p64f);
+    }
+    if (__any(bad) && (threadIdx.x & (kWave - 1)) == 0) *sm.rerun = 1;
+    __syncthreads();
+    if (*sm.rerun) {
+        init_state<D>(st);
+        attend_range<D, true>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
+                              sm);
+    }
 }
 
 // ---------------------------------------------------------------- prefill
@@ -746,12 +895,15 @@ __device__ inline int xcd_remap(int L, int N) {
     return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
-#define DECLARE_TILE_SMEM(D)                                              \
-    __shared__ __attribute__((aligned(1024))) u16 sk0[kBN * (D)];        \
-    __shared__ __attribute__((aligned(1024))) u16 sv0[kBN * (D)];        \
-    __shared__ __attribute__((aligned(1024))) u16 sk1[kBN * (D)];        \
-    __shared__ __attribute__((aligned(1024))) u16 sv1[kBN * (D)];        \
-    const TileSmem<D> sm{sk0, sv0, sk1, sv1}
+#define DECLARE_TILE_SMEM(D)                                                              \
+    __shared__ __attribute__((aligned(1024))) u16 sk0[kBN * (D)];                        \
+    __shared__ __attribute__((aligned(1024))) u16 sv0[kBN * (D)];                        \
+    __shared__ __attribute__((aligned(1024))) u16 sk1[kBN * (D)];                        \
+    __shared__ __attribute__((aligned(1024))) u16 sv1[kBN * (D)];                        \
+    __shared__ __attribute__((aligned(1024))) u16 sk2[kBN * (D)];                        \
+    __shared__ __attribute__((aligned(1024))) u16 sv2[kBN * (D)];                        \
+    __shared__ int rerun_flag;                                                           \
+    const TileSmem<D> sm{{sk0, sk1, sk2}, {sv0, sv1, sv2}, &rerun_flag}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
@@ -802,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     init_state<D>(st);
     KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
               a.vs[2]};
-    attend_range<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, sm);
+    attend<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1004,7 +1156,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     init_state<D>(st);
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
               a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R};
-    attend_range<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
+    attend<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1141,6 +1293,8 @@ int check_layout(const char* name, const void* p, const int64_t* str, int n) {
     return ATTN_OK;
 }
 
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Key splits of a prefill launch: enough workgroups to fill every compute
@@ -1234,6 +1388,9 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     if ((st = check_layout("k", k, k_str, 4))) return st;
     if ((st = check_layout("v", v, v_str, 4))) return st;
     if ((st = check_layout("out", out, o_str, 4))) return st;
+    // tile copies address the rows of a 64-key tile with 32-bit byte offsets
+    if (k_str[2] >= kMaxRowStride || v_str[2] >= kMaxRowStride)
+        return fail(ATTN_ERR_UNSUPPORTED, "k/v row stride must be below 2^24 elements");
     const int64_t qsz[4] = {B, Hq, Lq, D}, ksz[4] = {B, Hkv, Lkv, D};
     if (!offset_ok(qsz, q_str, 4) || !offset_ok(ksz, k_str, 4) || !offset_ok(ksz, v_str, 4) ||
         !offset_ok(qsz, o_str, 4))

@@ -74,6 +74,8 @@ def _prefill(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64, scale=0
     (dict(qs=_s(4 * 8 * 64, 8 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),   # inner stride
     (dict(ks=_s(2 * 16 * 64, 16 * 64, 68, 1)), attn.ATTN_ERR_UNSUPPORTED),  # row not 16 B
     (dict(vs=_s(2 * 16 * 64, -16 * 64, 64, 1)), attn.ATTN_ERR_UNSUPPORTED),  # negative
+    (dict(ks=_s(2 * 16 << 24, 16 << 24, 1 << 24, 1)), attn.ATTN_ERR_UNSUPPORTED),  # row 2^24
+    (dict(vs=_s(2 * 16 << 25, 16 << 25, 1 << 25, 1)), attn.ATTN_ERR_UNSUPPORTED),
     (dict(out=A + 8), attn.ATTN_ERR_UNSUPPORTED),                           # misaligned
     (dict(k=A + 2), attn.ATTN_ERR_UNSUPPORTED),
 ])

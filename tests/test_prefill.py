@@ -152,3 +152,66 @@ def test_full_size_strided_output():
     rows = sample_rows(Lq, head=8, tail=8, every=509)
     ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D), rows=rows)
     compare(bshd.transpose(1, 2)[:, :, rows], ref, "BSHD full size")
+
+
+# ------------------------------------------- the fixed-reference pass and its rerun
+
+def _shifted_keys(k, q, scale, logit_of_key):
+    """K with each key moved along the all-ones direction so that its logit
+    against the mean query rises by logit_of_key[j] nats (q made positive, so
+    the shift is the same sign for every row)."""
+    qpos = q.abs()
+    qsum = qpos.float().sum(-1).mean().item()
+    shift = (logit_of_key / (scale * qsum)).view(1, 1, -1, 1)
+    return qpos, (k.float() + shift).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_logits_far_from_the_first_tile(D, direction):
+    """Logits that rise along the keys by ~150 nats overflow the reference
+    taken from the first tile, so the workgroups redo the range exactly;
+    falling logits stay on the fast pass with tiny P.  Both match the oracle."""
+    B, Hq, Hkv, Lq, Lkv = 1, 8, 2, 64, 2000
+    say("logits", direction, "D", D)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=25)
+    scale = 1.0 / math.sqrt(D)
+    ramp = torch.linspace(0.0, 150.0, Lkv)
+    if direction == "falling":
+        ramp = ramp.flip(0)
+    q, k = _shifted_keys(k, q, scale, ramp)
+    out = _run(q, k, v, scale=scale)
+    ref = oracle.prefill(q, k, v, scale)
+    compare(out, ref, "logits %s D %d" % (direction, D))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_rising_logits_with_splits(splits, monkeypatch):
+    """Each split keeps its own reference; splits whose logits outgrow it are
+    redone exactly and the merge combines both kinds of partials."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
+    B, Hq, Hkv, Lq, Lkv, D = 1, 8, 2, 96, 3000, 128
+    say("rising logits, splits", splits)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=26)
+    scale = 1.0 / math.sqrt(D)
+    ramp = torch.zeros(Lkv)
+    ramp[2000:] = torch.linspace(0.0, 200.0, Lkv - 2000)  # only the last split outgrows
+    q, k = _shifted_keys(k, q, scale, ramp)
+    out = _run(q, k, v, scale=scale)
+    ref = oracle.prefill(q, k, v, scale)
+    compare(out, ref, "rising logits, splits %d" % splits)
+
+
+def test_windowed_rows_with_very_negative_logits():
+    """Rows whose window starts past the first tile keep the reference 0; with
+    every logit near -150 nats their sums underflow and the workgroup redoes
+    the range exactly."""
+    B, Hq, Hkv, Lq, Lkv, D = 1, 8, 2, 128, 1000, 64
+    say("windowed, very negative logits")
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=27)
+    scale = 1.0 / math.sqrt(D)
+    q, k = _shifted_keys(k, q, scale, torch.full((Lkv,), -150.0))
+    out = _run(q, k, v, scale=scale, window=64)
+    ref = oracle.prefill(q, k, v, scale, window=64)
+    compare(out, ref, "windowed negative logits")
+    assert torch.isfinite(out).all()
