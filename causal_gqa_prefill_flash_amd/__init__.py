@@ -54,6 +54,10 @@ def lib():
                                    I, I, I, I64A, I64A, I64A, I64A, P, SZ, P]
     L.attn_varlen_read_error.restype = I
     L.attn_varlen_read_error.argtypes = [P, I, I, P, ctypes.POINTER(ctypes.c_int32)]
+    L.attn_timing_begin.restype = I
+    L.attn_timing_begin.argtypes = []
+    L.attn_timing_end.restype = I
+    L.attn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
     _lib = L
     return L
 
@@ -192,3 +196,16 @@ def varlen_read_error(workspace, S, T):
     e = ctypes.c_int32(0)
     _check(lib().attn_varlen_read_error(_ptr(workspace), S, T, _stream(), ctypes.byref(e)))
     return e.value
+
+
+def timing_begin():
+    """Start recording HIP events around the attention kernel of every call
+    made on this thread (a profiling aid)."""
+    _check(lib().attn_timing_begin())
+
+
+def timing_end():
+    """Stop recording; returns (summed attention-kernel ms, launches)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(lib().attn_timing_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

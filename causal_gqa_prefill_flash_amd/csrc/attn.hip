@@ -33,6 +33,8 @@
 #include <string.h>
 
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "attn.h"
 
@@ -1236,6 +1238,47 @@ int fail(int code, const char* fmt, ...) {
 
 void clear_err() { g_err[0] = 0; }
 
+// Optional timing of the attention kernels (attn_timing_begin / _end): HIP
+// event pairs recorded on the launch stream around each attention kernel,
+// per host thread.  Events are reused across begin/end rounds.
+struct Timing {
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> marks;
+    std::vector<hipEvent_t> pool;
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+    }
+    void recycle() {
+        for (auto& m : marks) {
+            if (m.first) pool.push_back(m.first);
+            if (m.second) pool.push_back(m.second);
+        }
+        marks.clear();
+    }
+};
+thread_local Timing g_timing;
+
+// Records the start event of a timed launch (nullptr when timing is off).
+hipEvent_t timing_start(hipStream_t s) {
+    if (!g_timing.on) return nullptr;
+    hipEvent_t e = g_timing.get();
+    if (e && hipEventRecord(e, s) != hipSuccess) e = nullptr;
+    return e;
+}
+
+void timing_stop(hipEvent_t start, hipStream_t s) {
+    if (!start) return;
+    hipEvent_t e = g_timing.get();
+    if (e && hipEventRecord(e, s) != hipSuccess) e = nullptr;
+    g_timing.marks.push_back({start, e});
+}
+
 struct DeviceInfo {
     int cus;
 };
@@ -1441,10 +1484,12 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     a.n_inner = (int)n_inner;
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)nwg);
+    hipEvent_t t0 = timing_start(s);
     if (D == 64)
         hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    timing_stop(t0, s);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed");
     if (nsplit > 1) {
         int64_t rows = (int64_t)B * Hq * Lq;
@@ -1556,10 +1601,12 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
         return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
     if (gx > 0 && T > 0 && S > 0) {
         dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)nsplit);
+        hipEvent_t t0 = timing_start(s);
         if (D == 64)
             hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(kThreads), 0, s, a);
         else
             hipLaunchKernelGGL(varlen_kernel<128>, grid, dim3(kThreads), 0, s, a);
+        timing_stop(t0, s);
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen launch failed");
     }
     dim3 fgrid((unsigned)varlen_finish_blocks(T));
@@ -1590,6 +1637,36 @@ int attn_varlen_read_error(const void* workspace, int S, int T, void* stream, in
     free(host);
     *err_out = e;
     return ATTN_OK;
+}
+
+int attn_timing_begin(void) {
+    clear_err();
+    g_timing.recycle();
+    g_timing.on = true;
+    return ATTN_OK;
+}
+
+int attn_timing_end(double* kernel_ms, int* launches) {
+    clear_err();
+    if (!kernel_ms || !launches) return fail(ATTN_ERR_INVALID, "null output pointer");
+    g_timing.on = false;
+    double total = 0.0;
+    int n = 0;
+    int st = ATTN_OK;
+    for (auto& m : g_timing.marks) {
+        float ms = 0.f;
+        if (!m.first || !m.second || hipEventSynchronize(m.second) != hipSuccess ||
+            hipEventElapsedTime(&ms, m.first, m.second) != hipSuccess) {
+            st = fail(ATTN_ERR_HIP, "a timing event could not be read");
+            continue;
+        }
+        total += ms;
+        ++n;
+    }
+    g_timing.recycle();
+    *kernel_ms = total;
+    *launches = n;
+    return st;
 }
 
 }  // extern "C"

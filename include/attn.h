@@ -150,6 +150,20 @@ int attn_sdpa_varlen(const void *q, const void *k_store, const void *v_store, vo
 int attn_varlen_read_error(const void *workspace, int S, int T, void *stream,
                            int32_t *err_out);
 
+/*
+ * Profiling aid (not part of the computation).  After attn_timing_begin(),
+ * every attn_causal_prefill / attn_sdpa_varlen call made on the same host
+ * thread records a pair of HIP events on its stream around its attention
+ * kernel (the split-merge and finish kernels are not included).
+ * attn_timing_end() waits for those events, writes the summed kernel time in
+ * milliseconds and the number of timed launches, and stops recording.  Events
+ * are created on first use and reused; nothing is allocated on the device.
+ * Returns ATTN_ERR_INVALID for null outputs, ATTN_ERR_HIP if an event could
+ * not be read (the others are still summed).
+ */
+int attn_timing_begin(void);
+int attn_timing_end(double *kernel_ms, int *launches);
+
 #ifdef __cplusplus
 }
 #endif

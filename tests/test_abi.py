@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -180,3 +180,12 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
     with pytest.raises(ImportError):
         attn.lib()
+
+
+def test_timing_end_rejects_null_outputs_and_counts_nothing_when_idle():
+    L = _lib()
+    assert L.attn_timing_begin() == attn.ATTN_OK
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int(-1)
+    assert L.attn_timing_end(ctypes.byref(ms), ctypes.byref(n)) == attn.ATTN_OK
+    assert ms.value == 0.0 and n.value == 0
+    assert L.attn_timing_end(None, ctypes.byref(n)) == attn.ATTN_ERR_INVALID
