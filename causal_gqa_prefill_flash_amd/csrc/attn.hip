@@ -191,13 +191,13 @@ struct TileCopyFlat {
     u16* dst;
     const uint32_t* o;
     __device__ TileCopyFlat(const KVFlat&, const u16* tb, int64_t rs, int rs2,
-                            const CopyOffsets<D>& co, int64_t k0, int k_hi, u16* d)
+                            const CopyOffsets<D>& co, int k0, int k_hi, u16* d)
         : dst(d), o(co.o) {
-        const int64_t nl = k_hi - k0;
-        const int nv = nl < 0 ? 0 : (nl > kBN ? kBN : (int)nl);
+        // 32-bit scalar arithmetic, no branches (k0 <= k_hi)
+        const int nv = min(k_hi - k0, kBN);
         const uint32_t nrec = nv > 0 ? (uint32_t)((nv - 1) * rs2 + 2 * D) : 0u;
 #if defined(__HIP_DEVICE_COMPILE__)
-        r = __builtin_amdgcn_make_buffer_rsrc((void*)(tb + (nv > 0 ? k0 : 0) * rs), 0,
+        r = __builtin_amdgcn_make_buffer_rsrc((void*)(tb + (int64_t)(nv > 0 ? k0 : 0) * rs), 0,
                                               nrec, 0x00020000);
 #else
         (void)tb, (void)rs, (void)nrec;
@@ -224,9 +224,9 @@ struct TileCopyRing {
     int R, kc, last;
     u16* dst;
     __device__ TileCopyRing(const KVRing& kv, const u16* t, int64_t s, int, const CopyOffsets<D>&,
-                            int64_t k0, int k_hi, u16* d)
+                            int k0, int k_hi, u16* d)
         : tb(t), rs(s), R(kv.R), dst(d) {
-        kc = k0 < k_hi ? (int)k0 : k_hi - 1;
+        kc = k0 < k_hi ? k0 : k_hi - 1;
         last = k_hi - 1 - kc;
     }
     __device__ void issue(int i) const {
@@ -522,11 +522,13 @@ template <int D, class KV>
 struct KeyLoop {
     KV kv;
     int k_lo, k_hi;
+    int n;                     // tiles in the range
     int ks2, vs2;              // row strides in bytes (flat storage: below 2^25)
     CopyOffsets<D> kco, vco;   // per-lane copy offsets (full tiles)
     int t_in0, t_in1;          // tiles t_in0 <= t < t_in1 need no mask
     __device__ int k0(int t) const { return k_lo + t * kBN; }
-    __device__ int64_t k0l(int t) const { return (int64_t)k_lo + (int64_t)t * kBN; }
+    // first key of a copied tile: k_hi for tiles past the range (nothing to copy)
+    __device__ int k0c(int t) const { return t < n ? k_lo + t * kBN : k_hi; }
     // a tile straddles a causal, window or range edge of some row
     __device__ bool needs_mask(int t) const { return t < t_in0 || t >= t_in1; }
 };
@@ -641,30 +643,35 @@ __device__ inline void copy_wait_barrier() {
 
 template <int D, class KV>
 __device__ inline typename TileCopySel<D, KV>::T k_copy(const KeyLoop<D, KV>& L, int t, u16* dst) {
-    return typename TileCopySel<D, KV>::T(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.kco, L.k0l(t), L.k_hi,
+    return typename TileCopySel<D, KV>::T(L.kv, L.kv.kb, L.kv.ks, L.ks2, L.kco, L.k0c(t), L.k_hi,
                                           dst);
 }
 template <int D, class KV>
 __device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L, int t, u16* dst) {
-    return typename TileCopySel<D, KV>::T(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.vco, L.k0l(t), L.k_hi,
+    return typename TileCopySel<D, KV>::T(L.kv, L.kv.vb, L.kv.vs, L.vs2, L.vco, L.k0c(t), L.k_hi,
                                           dst);
 }
 
 // One ping-pong step for tile k >= 1: the MFMA phase M(k) (scores of tile k
-// from Kr, PV of tile k-1 from Vr) with the copies of K(k+2) into Kw and
-// V(k+1) into Vw, then the softmax phase of tile k, each closed by a
-// workgroup barrier.  At the end of M(k) every wave waits for its copies of
-// the previous step (K(k+1), V(k)); those of this step stay in flight.
+// from Kr, PV of tile k-1 from Vr) with the copies ck of K(k+2) and cv of
+// V(k+1), then the softmax phase of tile k, each closed by a workgroup
+// barrier.  At the end of M(k) every wave waits for its copies of the
+// previous step (K(k+1), V(k)); those of this step stay in flight.  The
+// softmax phase also prepares the next step's copy descriptors (K(k+3) into
+// Kn, V(k+2) into Vn): scalar work that would otherwise delay the first
+// MFMA of the next phase.
 template <int D, bool EXACT, class KV>
 __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
                                float c, const LaneBounds* lb, TileScores& S, TileP& pk,
-                               RowState<D>& st, const u16* Kr, const u16* Vr, u16* Kw, u16* Vw) {
+                               RowState<D>& st, const u16* Kr, const u16* Vr,
+                               typename TileCopySel<D, KV>::T& ck,
+                               typename TileCopySel<D, KV>::T& cv, u16* Kn, u16* Vn) {
     typedef typename TileCopySel<D, KV>::T TC;
-    const TC ck = k_copy<D>(L, k + 2, Kw);
-    const TC cv = v_copy<D>(L, k + 1, Vw);
     m_phase<D, true, true>(Kr, Vr, qf, S, pk, st, ck, cv);
     copy_wait_barrier<2 * TC::N>();
     v_phase<D, EXACT>(L, k, c, lb, S, pk, st);
+    ck = k_copy<D>(L, k + 3, Kn);
+    cv = v_copy<D>(L, k + 2, Vn);
     phase_barrier();
 }
 
@@ -703,6 +710,7 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     L.vco = copy_offsets<D>(L.vs2);
     interior_tiles<D>(L, causal, window, p_min, p_max);
     const int n = (k_hi - k_lo + kBN - 1) / kBN;
+    L.n = n;
     LaneBounds lb[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) lb[nt] = lane_bounds(k_lo, k_hi, causal, window, p_lane[nt]);
@@ -720,30 +728,34 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
             v0c.issue(i);
         }
     }
+    TC ck = k_copy<D>(L, 2, sm.k[2]), cv = v_copy<D>(L, 1, sm.v[1]);
     tile_barrier();
     if (g1) phase_barrier();  // group 1 runs one phase behind
-    {
-        // M(0): scores of tile 0, copies of K(2) and V(1)
-        const TC ck = k_copy<D>(L, 2, sm.k[2]), cv = v_copy<D>(L, 1, sm.v[1]);
-        qk_tile<D>(sm.k[0], qf, S, ck, cv);
-        pin_m_outputs<D>(S, st, true, false);
-        copy_wait_barrier<2 * TC::N>();
-    }
+    // M(0): scores of tile 0, copies of K(2) and V(1)
+    qk_tile<D>(sm.k[0], qf, S, ck, cv);
+    pin_m_outputs<D>(S, st, true, false);
+    copy_wait_barrier<2 * TC::N>();
     v_phase<D, true>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
+    ck = k_copy<D>(L, 3, sm.k[0]);
+    cv = v_copy<D>(L, 2, sm.v[2]);
     phase_barrier();
     int k = 1;
     for (; k + 2 < n; k += 3) {
-        // k = 1 mod 3: K(k) in stage 1, V(k-1) in stage 0; write K(k+2) -> 0, V(k+1) -> 2
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], sm.k[0], sm.v[2]);
-        pp_step<D, EXACT>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], sm.k[1], sm.v[0]);
-        pp_step<D, EXACT>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], sm.k[2], sm.v[1]);
+        // k = 1 mod 3: K(k) in stage 1, V(k-1) in stage 0; copies of K(k+2) -> 0,
+        // V(k+1) -> 2 (ck, cv); the next step's go to K stage 1, V stage 0
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
+        pp_step<D, EXACT>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
+                          sm.v[1]);
+        pp_step<D, EXACT>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck, cv, sm.k[0],
+                          sm.v[2]);
     }
     if (k < n) {
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], sm.k[0], sm.v[2]);
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
         ++k;
     }
     if (k < n) {
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], sm.k[1], sm.v[0]);
+        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
+                          sm.v[1]);
         ++k;
     }
     // M(n): PV of tile n-1, whose V sits in stage (n-1) % 3; then no copy
