@@ -54,6 +54,9 @@ constexpr int kBN = 64;           // keys per tile
 constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
 constexpr int kMaxSplits = 16;    // key splits of a prefill launch
 constexpr int kMaxVarlenSplits = 32;
+constexpr int kShortSplitKeys = 1024;  // short segments: keys per split, over the store rows
+constexpr int kLongSplitKeys = 512;    // longer segments: target keys per split of a q-block
+constexpr int kMaxLongSplits = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Rows of a workgroup: Gc query heads (of one GQA group) x P positions.
@@ -1058,9 +1061,11 @@ struct VarlenArgs {
     const int32_t* seq_info;
     const int32_t* seg_attr;
     int32_t* err;    // one word per finish workgroup
-    float* part_o;   // [S][qsplit][Hq][nsplit][D]
+    float* part_o;   // short segments: [S][qsplit][Hq][nsplit][D]
     float* part_ml;  // [S][qsplit][Hq][nsplit][2]
-    int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows, nsplit;
+    float* lpart_o;  // longer segments: [T][Hq][nlong][D]
+    float* lpart_ml; // [T][Hq][nlong][2]
+    int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows, nsplit, nlong;
     float c;
     int negate;
     int64_t qs[3], ks[4], vs[4], os[3];
@@ -1104,6 +1109,28 @@ __device__ inline bool seg_splits(const Segment& g, int qsplit, int nsplit) {
     return nsplit > 1 && g.q_len <= qsplit;
 }
 
+// Visible key range [lo, hi) of q-block qb (P positions) of segment g.
+__device__ inline void block_range(const Segment& g, int qb, int P, int64_t* lo, int64_t* hi,
+                                   int64_t* p_min, int64_t* p_max) {
+    const int64_t base = (int64_t)g.kv_end - g.q_len;
+    *p_min = base + (int64_t)qb * P;
+    *p_max = base + min(qb * P + P, g.q_len) - 1;
+    int64_t l = g.window > 0 ? *p_min - g.window + 1 : 0;
+    int64_t h = g.kv_end;
+    if (g.causal && *p_max + 1 < h) h = *p_max + 1;
+    if (l < 0) l = 0;
+    if (h < l) h = l;
+    *lo = l;
+    *hi = h;
+}
+
+// Key splits of a q-block of a segment longer than the short-split limit:
+// about kLongSplitKeys keys each, at most nlong.
+__device__ inline int long_splits(int64_t lo, int64_t hi, int nlong) {
+    const int64_t n = (hi - lo + kLongSplitKeys - 1) / kLongSplitKeys;
+    return n < 1 ? 1 : (n > nlong ? nlong : (int)n);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     DECLARE_TILE_SMEM(D);
@@ -1131,15 +1158,15 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
         blk -= nb;
     }
     if (seg < 0) return;
-    const bool splits = seg_splits(sg, qsplit, a.nsplit);
-    if (!splits && split > 0) return;
-    const int nsplit = splits ? a.nsplit : 1;
+    const bool short_split = seg_splits(sg, qsplit, a.nsplit);
+    int64_t lo64, hi64, p_min, p_max;
+    block_range(sg, qb, rm.P, &lo64, &hi64, &p_min, &p_max);
+    const int nsplit = short_split ? a.nsplit : long_splits(lo64, hi64, a.nlong);
+    if (split >= nsplit) return;
 
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int64_t base = (int64_t)sg.kv_end - sg.q_len;
-    const int64_t p_min = base + qb * rm.P;
-    const int64_t p_max = base + min(qb * rm.P + rm.P, sg.q_len) - 1;
 
     int hrow[kNT], jrow[kNT];
     bool valid[kNT];
@@ -1158,11 +1185,6 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
                   valid[nt], a.negate);
     }
 
-    int64_t lo64 = sg.window > 0 ? p_min - sg.window + 1 : 0;
-    int64_t hi64 = sg.kv_end;
-    if (sg.causal && p_max + 1 < hi64) hi64 = p_max + 1;
-    if (lo64 < 0) lo64 = 0;
-    if (hi64 < lo64) hi64 = lo64;
     int k_lo, k_hi;
     split_range((int)lo64, (int)hi64, split, nsplit, &k_lo, &k_hi);
 
@@ -1175,13 +1197,17 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const int t = sg.q_start + jrow[nt];
-        if (!splits) {
+        if (nsplit == 1) {
             store_out<D>(st.o[nt], st.l[nt], a.out + (int64_t)t * a.os[0] + (int64_t)hrow[nt] * a.os[1],
                          valid[nt]);
-        } else {
+        } else if (short_split) {
             const int64_t row = (((int64_t)seg * qsplit + jrow[nt]) * a.Hq + hrow[nt]) * a.nsplit + split;
             store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
                              a.part_ml + row * 2, valid[nt]);
+        } else {
+            const int64_t row = ((int64_t)t * a.Hq + hrow[nt]) * a.nlong + split;
+            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.lpart_o + row * D,
+                             a.lpart_ml + row * 2, valid[nt]);
         }
     }
 }
@@ -1216,17 +1242,28 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     if (t < a.T) {
         const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
         const Segment sg = owner >= 0 ? read_segment(a, owner) : Segment{};
-        if (owner < 0 || seg_splits(sg, qsplit, a.nsplit)) {
+        const bool short_split = owner >= 0 && seg_splits(sg, qsplit, a.nsplit);
+        int nlong = 1;
+        if (owner >= 0 && !short_split) {
+            int64_t lo, hi, pmn, pmx;
+            block_range(sg, (t - sg.q_start) / rm.P, rm.P, &lo, &hi, &pmn, &pmx);
+            nlong = long_splits(lo, hi, a.nlong);
+        }
+        if (owner < 0 || short_split || nlong > 1) {
             constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
             for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
                 const int h = e / TPR, d0 = (e % TPR) * 4;
                 u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
                 if (owner < 0) {
                     *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
-                } else {
+                } else if (short_split) {
                     const int64_t row =
                         (((int64_t)owner * qsplit + (t - sg.q_start)) * a.Hq + h) * a.nsplit;
                     combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, a.nsplit, d0,
+                                   orow);
+                } else {
+                    const int64_t row = ((int64_t)t * a.Hq + h) * a.nlong;
+                    combine_row<D>(a.lpart_o + row * D, a.lpart_ml + row * 2, D, 2, nlong, d0,
                                    orow);
                 }
             }
@@ -1385,9 +1422,19 @@ size_t prefill_ws_bytes(int B, int Hq, int Lq, int D, int nsplit) {
 // about 256 keys per split over the rows a column can hold.
 int varlen_splits(int rows) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
-    int ns = forced > 0 ? forced : (rows + 255) / 256;
+    int ns = forced > 0 ? forced : (rows + kShortSplitKeys - 1) / kShortSplitKeys;
     if (ns < 1) ns = 1;
     if (ns > kMaxVarlenSplits) ns = kMaxVarlenSplits;
+    return ns;
+}
+
+// Split bound of the q-blocks of longer segments (no segment sees more than
+// rows keys).
+int varlen_long_splits(int rows) {
+    int forced = env_int("ATTN_FORCE_LONG_SPLITS", 0);
+    int ns = forced > 0 ? forced : (rows + kLongSplitKeys - 1) / kLongSplitKeys;
+    if (ns < 1) ns = 1;
+    if (ns > kMaxLongSplits) ns = kMaxLongSplits;
     return ns;
 }
 
@@ -1397,11 +1444,17 @@ int varlen_finish_blocks(int T) { return T > 0 ? T : 1; }
 size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
     RowMap rm = row_map(Hq / Hkv);
     int qsplit = varlen_qsplit(rm.P);
-    int ns = varlen_splits(rows);
-    size_t err = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
-    if (ns <= 1) return err;
-    size_t prow = (size_t)(S > 0 ? S : 0) * qsplit * Hq * ns;
-    return err + align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
+    int ns = varlen_splits(rows), nl = varlen_long_splits(rows);
+    size_t bytes = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
+    if (ns > 1) {
+        size_t prow = (size_t)(S > 0 ? S : 0) * qsplit * Hq * ns;
+        bytes += align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
+    }
+    if (nl > 1) {
+        size_t prow = (size_t)(T > 0 ? T : 0) * Hq * nl;
+        bytes += align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
+    }
+    return bytes;
 }
 
 }  // namespace
@@ -1568,7 +1621,7 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     DeviceInfo di;
     if ((st = device_info(&di))) return st;
 
-    const int nsplit = varlen_splits(rows);
+    const int nsplit = varlen_splits(rows), nlong = varlen_long_splits(rows);
     RowMap rm = row_map(Hq / Hkv);
     const int qsplit = varlen_qsplit(rm.P);
     VarlenArgs a;
@@ -1581,9 +1634,20 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.err = (int32_t*)workspace;
     size_t errb = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
     size_t prow = (size_t)S * qsplit * Hq * nsplit;
-    a.part_o = nsplit > 1 ? (float*)((char*)workspace + errb) : nullptr;
-    a.part_ml = nsplit > 1 ? (float*)((char*)workspace + errb + align256(prow * D * sizeof(float)))
-                           : nullptr;
+    char* wp = (char*)workspace + errb;
+    a.part_o = a.part_ml = a.lpart_o = a.lpart_ml = nullptr;
+    if (nsplit > 1) {
+        a.part_o = (float*)wp;
+        wp += align256(prow * D * sizeof(float));
+        a.part_ml = (float*)wp;
+        wp += align256(prow * 2 * sizeof(float));
+    }
+    if (nlong > 1) {
+        size_t lrow = (size_t)T * Hq * nlong;
+        a.lpart_o = (float*)wp;
+        wp += align256(lrow * D * sizeof(float));
+        a.lpart_ml = (float*)wp;
+    }
     a.S = S;
     a.T = T;
     a.Hq = Hq;
@@ -1594,6 +1658,7 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.window = window;
     a.ring_rows = ring_rows;
     a.nsplit = nsplit;
+    a.nlong = nlong;
     // c > 0 keeps exp2(-inf * c) = 0 for masked scores; a zero scale gives
     // weights that round to exactly 1 (uniform)
     a.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
@@ -1612,7 +1677,7 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     if (gx > 0x7fffffff || gy > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
     if (gx > 0 && T > 0 && S > 0) {
-        dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)nsplit);
+        dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)(nsplit > nlong ? nsplit : nlong));
         hipEvent_t t0 = timing_start(s);
         if (D == 64)
             hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(kThreads), 0, s, a);

@@ -70,6 +70,45 @@ def test_short_query_steps_split_keys(D):
     compare(out, ref, "short steps D%d" % D)
 
 
+@pytest.mark.parametrize("long_splits", [1, 2, 5, 8])
+def test_long_segments_split_keys(long_splits, monkeypatch):
+    """q-blocks of segments longer than a decode step split their visible keys
+    (about 512 a split by default); any split count merges to the oracle."""
+    monkeypatch.setenv("ATTN_FORCE_LONG_SPLITS", str(long_splits))
+    say("varlen long splits", long_splits)
+    st = synth.VARLEN_STORE
+    info, attr, T = synth.pinned_varlen_table()
+    q, ks, vs = synth.varlen_inputs(T, st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"],
+                                    wid=46)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
+    assert err == 0
+    compare(out, ref, "long splits %d" % long_splits)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_long_segment_rising_logits_split(D):
+    """Logits that rise by ~200 nats over the last keys of a long segment make
+    the later splits of each q-block redo their ranges exactly; the merge takes
+    fast-pass and exact partials together."""
+    say("varlen long segment, rising logits, D", D)
+    rows, cols, Hkv, Hq = 4096, 3, 2, 16
+    q_len, kv_end = 200, 4000
+    q, ks, vs = synth.varlen_inputs(q_len + 8, rows, cols, Hkv, D, Hq, wid=47)
+    scale = 1.0 / math.sqrt(D)
+    q = q.abs()
+    qsum = q.float().sum(-1).mean().item()
+    ramp = torch.zeros(rows)
+    ramp[2500:kv_end] = torch.linspace(0.0, 200.0, kv_end - 2500)
+    ks = (ks.float() + (ramp / (scale * qsum)).view(rows, 1, 1, 1)).to(torch.bfloat16)
+    info = torch.tensor([(4, q_len, 1, kv_end)], dtype=torch.int32)
+    out, err = _gpu_varlen(q, ks, vs, info, scale=scale)
+    ref = oracle.varlen(q, ks, vs, info, scale=scale)
+    assert err == 0
+    compare(out, ref, "long segment rising logits D%d" % D)
+    assert torch.count_nonzero(out[:4]) == 0 and torch.count_nonzero(out[4 + q_len:]) == 0
+
+
 def test_single_segment_equals_prefill_on_the_column_view():
     say("varlen vs prefill on a strided column")
     rows, cols, Hkv, D, Hq = 4096, 5, 2, 128, 16
