@@ -15,7 +15,14 @@ The roofline object prices the step against the bf16 dense MFMA peak, with
 the step time measured by HIP events on the stream the kernels run on.  The
 cpu_baseline object times the fp64 oracle on a bounded row sample of the same
 workload on the host cores.  Varlen workloads (--workload varlen_pinned,
-varlen_short) report HBM GB/s of algorithmic bytes instead.
+varlen_short) report HBM GB/s of algorithmic bytes instead; their step time
+comes from replaying a captured graph of 10 back-to-back launches that
+rotate over 8 copies of the store (more than the last-level cache holds).
+
+The roofline object also carries the average shader clock the timed
+attention workgroups ran at (per XCD too) and, for the MFMA peak, the
+fraction of the peak at that clock.  timing_protocol gives per-call median
+and min over 7 outer repetitions and the mean of repetitions 3 to 7.
 """
 import argparse
 import hashlib
@@ -89,7 +96,8 @@ def traffic_from_profile(workload):
 
 def time_calls(fn, steps, warmup):
     """(ms per step from events around the whole timed loop, ms per launch of
-    the attention kernel from the library's own events on its stream)."""
+    the attention kernel from the library's own events on its stream, the
+    shader clock those launches ran at)."""
     import causal_gqa_prefill_flash_amd as attn
     for _ in range(warmup):
         fn()
@@ -103,7 +111,93 @@ def time_calls(fn, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     kernel_ms, launches = attn.timing_end()
-    return start.elapsed_time(end) / steps, kernel_ms / max(launches, 1)
+    return start.elapsed_time(end) / steps, kernel_ms / max(launches, 1), clock_info()
+
+
+def clock_info():
+    """Average shader clock of the last timed launches (per XCD too), from the
+    library's cycle and reference-tick sums."""
+    import causal_gqa_prefill_flash_amd as attn
+    try:
+        mhz, per = attn.timing_clock()
+    except RuntimeError as e:
+        return {"sclk_mhz": None, "error": str(e)}
+    return {"sclk_mhz": round(mhz, 1), "sclk_per_xcd_mhz": [round(x, 1) for x in per]}
+
+
+def with_clock(roof, clk, peak, peak_clock_mhz=2400.0):
+    """Adds the measured clock and, for a compute peak (which scales with the
+    clock), the fraction of that peak at the measured clock."""
+    roof.update(clk)
+    if peak and clk.get("sclk_mhz"):
+        p = peak * clk["sclk_mhz"] / peak_clock_mhz
+        roof["peak_at_sclk"] = round(p, 1)
+        roof["frac_at_sclk"] = round(roof["achieved"] / p, 4)
+    return roof
+
+
+def protocol_stats(fn, steps, reps=7):
+    """Per-call times over `reps` outer repetitions of `steps` calls (events
+    around each call): median and min over all calls, each repetition's mean,
+    and the mean of repetitions 3..7."""
+    evs = []
+    for _ in range(reps):
+        row = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            row.append((a, b))
+        evs.append(row)
+    torch.cuda.synchronize()
+    per = [[a.elapsed_time(b) for a, b in row] for row in evs]
+    flat = sorted(x for row in per for x in row)
+    means = [sum(row) / len(row) for row in per]
+    return {"per_call_ms_median": round(flat[len(flat) // 2], 4),
+            "per_call_ms_min": round(flat[0], 4),
+            "rep_mean_ms": [round(m, 4) for m in means],
+            "mean_of_reps_3_to_7_ms": round(sum(means[2:7]) / len(means[2:7]), 4),
+            "reps": reps, "calls_per_rep": steps}
+
+
+def time_graph(fns, steps, warmup):
+    """ms per launch of the varlen path replayed from captured graphs: one
+    graph of len(fns) back-to-back launches (fns[i] launches the i-th), plus
+    one of steps % len(fns) launches, so exactly `steps` launches are timed."""
+    n = len(fns)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    tail = None
+    if steps % n:
+        tail = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tail):
+            for f in fns[:steps % n]:
+                f()
+    torch.cuda.synchronize()
+    for _ in range(max(1, (warmup + n - 1) // n)):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps // n):
+        g.replay()
+    if tail is not None:
+        tail.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
 
 
 def cpu_baseline_prefill(q, k, v, w, budget_s=12.0):
@@ -146,7 +240,8 @@ def bench_prefill(args, name):
     def step():
         attn.causal_prefill(q, k, v, out=out, q_pos0=q_pos0, workspace=ws)
 
-    ms, kms = time_calls(step, args.steps, args.warmup)
+    ms, kms, clk = time_calls(step, args.steps, args.warmup)
+    proto = protocol_stats(step, args.steps)
     pairs = prefill_pairs(B, Hq, Lq, Lkv, q_pos0, 0)
     flops = 4.0 * D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -160,14 +255,17 @@ def bench_prefill(args, name):
                    "D": D, "Lq": Lq, "Lkv": Lkv, "q_pos0": q_pos0,
                    "unmasked_pairs": pairs},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(ktflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ktflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(name),
-                     "kernel": "prefill_kernel<%d>" % D,
-                     "kernel_ms_per_launch": round(kms, 4),
-                     "algorithmic_flop_per_launch": flops,
-                     "timed": "attention kernel alone: HIP events recorded by the library on "
-                              "its launch stream around every launch of the timed loop"},
+        "roofline": with_clock(
+            {"bound": "mfma", "achieved": round(ktflops, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(ktflops / PEAK_BF16_TFLOPS, 4),
+             "traffic": traffic_from_profile(name),
+             "kernel": "prefill_kernel<%d>" % D,
+             "kernel_ms_per_launch": round(kms, 4),
+             "algorithmic_flop_per_launch": flops,
+             "timed": "attention kernel alone: HIP events recorded by the library on "
+                      "its launch stream around every launch of the timed loop"},
+            clk, PEAK_BF16_TFLOPS),
+        "timing_protocol": proto,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(qc, kc, vc, w)
@@ -210,7 +308,15 @@ def bench_varlen(args, name):
         it[0] += 1
         attn.sdpa_varlen(q, ks, vs, si, seg_attr=sa, out=out, workspace=ws)
 
-    ms, kms = time_calls(step, args.steps, args.warmup)
+    def launch(c):
+        ks, vs = stores[c % ncopy]
+        return lambda: attn.sdpa_varlen(q, ks, vs, si, seg_attr=sa, out=out, workspace=ws)
+
+    # the step time: a captured graph of 10 back-to-back launches, each on
+    # the next store copy; the kernel time and clock: an eager pass with the
+    # library's events around the attention kernel
+    ms = time_graph([launch(c) for c in range(10)], args.steps, args.warmup)
+    eager_ms, kms, clk = time_calls(step, args.steps, args.warmup)
     pairs, kv_rows = varlen_pairs_and_bytes(info, attr, Hq, Hkv, D)
     nbytes = kv_rows * Hkv * D * 2 * 2 + T * Hq * D * 2 * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -220,14 +326,19 @@ def bench_varlen(args, name):
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "timed": "graph replay: one captured graph of 10 back-to-back launches, each on the "
+                 "next of %d store copies; ms_per_step = graph time / 10" % ncopy,
+        "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": name, "rows": rows, "cols": cols, "Hkv": Hkv, "D": D, "Hq": Hq,
                    "T": T, "S": int(info.shape[0]), "unmasked_pairs": pairs,
                    "store_copies_rotated": ncopy},
-        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile(name), "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": "varlen_kernel<%d>" % D, "kernel_ms_per_launch": round(kms, 4),
-                     "tflops_unmasked": round(4.0 * D * pairs / (ms * 1e-3) / 1e12, 3)},
+        "roofline": with_clock(
+            {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
+             "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+             "traffic": traffic_from_profile(name), "algorithmic_bytes_per_launch": nbytes,
+             "kernel": "varlen_kernel<%d>" % D, "kernel_ms_per_launch": round(kms, 4),
+             "tflops_unmasked": round(4.0 * D * pairs / (ms * 1e-3) / 1e12, 3)},
+            clk, None),
     }
 
 

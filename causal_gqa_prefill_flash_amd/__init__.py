@@ -58,6 +58,8 @@ def lib():
     L.attn_timing_begin.argtypes = []
     L.attn_timing_end.restype = I
     L.attn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
+    L.attn_timing_clock.restype = I
+    L.attn_timing_clock.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     _lib = L
     return L
 
@@ -209,3 +211,11 @@ def timing_end():
     ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
     _check(lib().attn_timing_end(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def timing_clock():
+    """After ``timing_end``: (average shader clock in MHz over the timed
+    attention workgroups, list of 8 per-XCD values, 0 where none ran)."""
+    mhz, per = ctypes.c_double(0.0), (ctypes.c_double * 8)()
+    _check(lib().attn_timing_clock(ctypes.byref(mhz), per))
+    return mhz.value, list(per)

@@ -51,11 +51,9 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kNT = 1;                  // 32-row MFMA tiles of query rows per wave
 constexpr int kBM = kWaves * 32 * kNT;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
-constexpr int kQSplitMax = 16;    // varlen segments up to this q_len may split keys
 constexpr int kMaxSplits = 16;    // key splits of a prefill launch
-constexpr int kMaxVarlenSplits = 32;
-constexpr int kShortSplitKeys = 1024;  // short segments: keys per split, over the store rows
-constexpr int kLongSplitKeys = 512;    // longer segments: target keys per split of a q-block
+constexpr int kMaxVarlenSplits = 16;  // key splits of one varlen q-block
+constexpr int kVarlenSplitKeys = 512; // varlen: target keys per split of a q-block
 constexpr int kMaxLongSplits = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -72,7 +70,6 @@ __host__ __device__ inline RowMap row_map(int g) {
     return r;
 }
 
-__host__ __device__ inline int varlen_qsplit(int P) { return P < kQSplitMax ? P : kQSplitMax; }
 
 // ---------------------------------------------------------------- device helpers
 
@@ -886,6 +883,41 @@ __device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
 
 // ---------------------------------------------------------------- prefill
 
+// Shader-clock sampling for the timing aid.  Thread 0 of each workgroup reads
+// the shader cycle counter (s_memtime) and the constant 100 MHz reference
+// counter (s_memrealtime) when it starts and when it is done, and adds both
+// lifetimes to the sums of its XCD: clk[2x] shader cycles, clk[2x+1]
+// reference ticks.  The ratio is the average shader clock while the
+// workgroups ran.  clk is null unless timing is on.
+__device__ unsigned long long g_clock[16];
+
+struct ClockMark {
+    unsigned long long cyc, ref;
+};
+
+__device__ inline ClockMark clock_mark(const unsigned long long* clk) {
+    ClockMark m{0, 0};
+    if (clk) {  // uniform: the counters are read into scalar registers
+        m.cyc = __builtin_amdgcn_s_memtime();
+        m.ref = __builtin_amdgcn_s_memrealtime();
+    }
+    return m;
+}
+
+__device__ inline void clock_add(unsigned long long* clk, ClockMark m) {
+    if (clk) {
+        const unsigned long long cyc = __builtin_amdgcn_s_memtime();
+        const unsigned long long ref = __builtin_amdgcn_s_memrealtime();
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        xcc &= 7;
+        if (threadIdx.x == 0) {  // vector atomics from one lane
+            atomicAdd(clk + 2 * xcc, cyc - m.cyc);
+            atomicAdd(clk + 2 * xcc + 1, ref - m.ref);
+        }
+    }
+}
+
 struct PrefillArgs {
     const u16* q;
     const u16* k;
@@ -899,6 +931,7 @@ struct PrefillArgs {
     int negate;
     int64_t q_pos0;
     int64_t qs[4], ks[4], vs[4], os[4];
+    unsigned long long* clk;  // timing aid: per-XCD clock sums, or null
 };
 
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id.  Map
@@ -925,6 +958,7 @@ __device__ inline int xcd_remap(int L, int N) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     DECLARE_TILE_SMEM(D);
+    const ClockMark cm = clock_mark(a.clk);
 
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
@@ -986,6 +1020,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                              a.part_ml + row * 2, valid[nt]);
         }
     }
+    clock_add(a.clk, cm);
 }
 
 // Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
@@ -1061,14 +1096,15 @@ struct VarlenArgs {
     const int32_t* seq_info;
     const int32_t* seg_attr;
     int32_t* err;    // one word per finish workgroup
-    float* part_o;   // short segments: [S][qsplit][Hq][nsplit][D]
-    float* part_ml;  // [S][qsplit][Hq][nsplit][2]
-    float* lpart_o;  // longer segments: [T][Hq][nlong][D]
-    float* lpart_ml; // [T][Hq][nlong][2]
-    int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows, nsplit, nlong;
+    float* part_o;   // split partials per packed row: [T][Hq][nsplit][D]
+    float* part_ml;  // [T][Hq][nsplit][2]
+    int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows;
+    int nsplit;      // most key splits of a q-block
+    int split_keys;  // target keys per split
     float c;
     int negate;
     int64_t qs[3], ks[4], vs[4], os[3];
+    unsigned long long* clk;  // timing aid: per-XCD clock sums, or null
 };
 
 struct Segment {
@@ -1105,10 +1141,6 @@ __device__ inline Segment read_segment(const VarlenArgs& a, int s) {
     return g;
 }
 
-__device__ inline bool seg_splits(const Segment& g, int qsplit, int nsplit) {
-    return nsplit > 1 && g.q_len <= qsplit;
-}
-
 // Visible key range [lo, hi) of q-block qb (P positions) of segment g.
 __device__ inline void block_range(const Segment& g, int qb, int P, int64_t* lo, int64_t* hi,
                                    int64_t* p_min, int64_t* p_max) {
@@ -1124,45 +1156,97 @@ __device__ inline void block_range(const Segment& g, int qb, int P, int64_t* lo,
     *hi = h;
 }
 
-// Key splits of a q-block of a segment longer than the short-split limit:
-// about kLongSplitKeys keys each, at most nlong.
-__device__ inline int long_splits(int64_t lo, int64_t hi, int nlong) {
-    const int64_t n = (hi - lo + kLongSplitKeys - 1) / kLongSplitKeys;
-    return n < 1 ? 1 : (n > nlong ? nlong : (int)n);
+// Work items of one segment: each of its nqb q-blocks, for every (kv head,
+// head chunk) pair (hg of them), splits its visible keys into nsplit chunks
+// of about split_keys keys.  cost = 64-key tiles of its largest item, the
+// key by which items are ordered longest first.  The largest key range of a
+// segment's q-blocks is its first or its last one's (the range size is
+// monotone in the block index in every mode).
+struct SegPlan {
+    int nqb, nsplit, cost, count;
+};
+
+__device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int split_keys, int nsplit_max) {
+    SegPlan p{0, 1, 0, 0};
+    if (g.flags || g.q_len <= 0) return p;
+    p.nqb = (g.q_len + P - 1) / P;
+    int64_t lo, hi, pmn, pmx, lo1, hi1;
+    block_range(g, 0, P, &lo, &hi, &pmn, &pmx);
+    block_range(g, p.nqb - 1, P, &lo1, &hi1, &pmn, &pmx);
+    const int64_t span = max(hi - lo, hi1 - lo1);
+    const int64_t n = (span + split_keys - 1) / split_keys;
+    p.nsplit = n < 1 ? 1 : (n > nsplit_max ? nsplit_max : (int)n);
+    p.cost = (int)min((int64_t)0x3fffffff, ((span + p.nsplit - 1) / p.nsplit + kBN - 1) / kBN);
+    p.count = p.nqb * hg * p.nsplit;
+    return p;
+}
+
+// The work item of linear index L: items are ordered by their segment's
+// cost, largest first (ties in table order), so the hardware dispatcher,
+// which starts workgroups in index order on whichever compute unit frees up,
+// schedules longest items first.  Each thread plans its own segments, then
+// sums the item counts of the segments ordered before them; one thread finds
+// the segment that holds L.  Returns false when L is past the last item.
+__device__ bool pick_item(const VarlenArgs& a, int P, int hg, int L, int* seg_out, int* j_out) {
+    constexpr int NT = kThreads;  // one segment per thread per pass
+    __shared__ int sh_cost[NT], sh_count[NT];
+    __shared__ int sh_seg, sh_j;
+    if (threadIdx.x == 0) sh_seg = -1;
+    for (int c0 = 0; c0 < a.S; c0 += NT) {
+        const int s = c0 + threadIdx.x;
+        const SegPlan ps = s < a.S ? seg_plan(read_segment(a, s), P, hg, a.split_keys, a.nsplit)
+                                   : SegPlan{0, 1, 0, 0};
+        int64_t off = 0;
+        for (int d0 = 0; d0 < a.S; d0 += NT) {
+            const int s2 = d0 + threadIdx.x;
+            SegPlan p2 = ps;
+            if (d0 != c0)
+                p2 = s2 < a.S ? seg_plan(read_segment(a, s2), P, hg, a.split_keys, a.nsplit)
+                              : SegPlan{0, 1, 0, 0};
+            __syncthreads();
+            sh_cost[threadIdx.x] = p2.cost;
+            sh_count[threadIdx.x] = p2.count;
+            __syncthreads();
+            const int n = min(NT, a.S - d0);
+            for (int i = 0; i < n; ++i) {
+                const int c2 = sh_cost[i];
+                if (c2 > ps.cost || (c2 == ps.cost && d0 + i < s)) off += sh_count[i];
+            }
+        }
+        if (s < a.S && ps.count > 0 && L >= off && L < off + ps.count) {
+            sh_seg = s;
+            sh_j = (int)(L - off);
+        }
+    }
+    __syncthreads();
+    *seg_out = sh_seg;
+    *j_out = sh_j;
+    return sh_seg >= 0;
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     DECLARE_TILE_SMEM(D);
+    const ClockMark cm = clock_mark(a.clk);
 
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
-    const int qsplit = varlen_qsplit(rm.P);
-    const int hk = blockIdx.y / rm.hchunks, hc = blockIdx.y % rm.hchunks;
-    const int split = blockIdx.z;
+    const int hg = a.Hkv * rm.hchunks;
 
-    // the (segment, q-block) of this workgroup: blocks are numbered through
-    // the valid segments in table order
-    int blk = blockIdx.x, seg = -1, qb = 0;
-    Segment sg;
-    for (int s = 0; s < a.S; ++s) {
-        Segment x = read_segment(a, s);
-        if (x.flags) continue;
-        int nb = (x.q_len + rm.P - 1) / rm.P;
-        if (blk < nb) {
-            seg = s;
-            qb = blk;
-            sg = x;
-            break;
-        }
-        blk -= nb;
-    }
-    if (seg < 0) return;
-    const bool short_split = seg_splits(sg, qsplit, a.nsplit);
+    // this workgroup's work item: (segment, item j of that segment)
+    int seg, j;
+    if (!pick_item(a, rm.P, hg, blockIdx.x, &seg, &j)) return;
+    const Segment sg = read_segment(a, seg);
+    const SegPlan pl = seg_plan(sg, rm.P, hg, a.split_keys, a.nsplit);
+    // item j: q-blocks from the last (the longest under causal masking),
+    // then split, then (kv head, head chunk)
+    const int per_qb = hg * pl.nsplit;
+    const int qb = pl.nqb - 1 - j / per_qb;
+    const int split = (j % per_qb) / hg, hy = j % hg;
+    const int hk = hy / rm.hchunks, hc = hy % rm.hchunks;
+    const int nsplit = pl.nsplit;
     int64_t lo64, hi64, p_min, p_max;
     block_range(sg, qb, rm.P, &lo64, &hi64, &p_min, &p_max);
-    const int nsplit = short_split ? a.nsplit : long_splits(lo64, hi64, a.nlong);
-    if (split >= nsplit) return;
 
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -1200,16 +1284,13 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
         if (nsplit == 1) {
             store_out<D>(st.o[nt], st.l[nt], a.out + (int64_t)t * a.os[0] + (int64_t)hrow[nt] * a.os[1],
                          valid[nt]);
-        } else if (short_split) {
-            const int64_t row = (((int64_t)seg * qsplit + jrow[nt]) * a.Hq + hrow[nt]) * a.nsplit + split;
+        } else {
+            const int64_t row = ((int64_t)t * a.Hq + hrow[nt]) * a.nsplit + split;
             store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
                              a.part_ml + row * 2, valid[nt]);
-        } else {
-            const int64_t row = ((int64_t)t * a.Hq + hrow[nt]) * a.nlong + split;
-            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.lpart_o + row * D,
-                             a.lpart_ml + row * 2, valid[nt]);
         }
     }
+    clock_add(a.clk, cm);
 }
 
 // Finish pass, one packed row per workgroup: merge split partials, zero a
@@ -1220,7 +1301,6 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     __shared__ int flags_sh, owner_sh, count_sh;
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
-    const int qsplit = varlen_qsplit(rm.P);
     const int t = blockIdx.x;
     if (threadIdx.x == 0) {
         flags_sh = 0;
@@ -1241,30 +1321,20 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     __syncthreads();
     if (t < a.T) {
         const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
-        const Segment sg = owner >= 0 ? read_segment(a, owner) : Segment{};
-        const bool short_split = owner >= 0 && seg_splits(sg, qsplit, a.nsplit);
-        int nlong = 1;
-        if (owner >= 0 && !short_split) {
-            int64_t lo, hi, pmn, pmx;
-            block_range(sg, (t - sg.q_start) / rm.P, rm.P, &lo, &hi, &pmn, &pmx);
-            nlong = long_splits(lo, hi, a.nlong);
-        }
-        if (owner < 0 || short_split || nlong > 1) {
+        int ns = 1;
+        if (owner >= 0)
+            ns = seg_plan(read_segment(a, owner), rm.P, a.Hkv * rm.hchunks, a.split_keys, a.nsplit)
+                     .nsplit;
+        if (owner < 0 || ns > 1) {
             constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
             for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
                 const int h = e / TPR, d0 = (e % TPR) * 4;
                 u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
                 if (owner < 0) {
                     *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
-                } else if (short_split) {
-                    const int64_t row =
-                        (((int64_t)owner * qsplit + (t - sg.q_start)) * a.Hq + h) * a.nsplit;
-                    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, a.nsplit, d0,
-                                   orow);
                 } else {
-                    const int64_t row = ((int64_t)t * a.Hq + h) * a.nlong;
-                    combine_row<D>(a.lpart_o + row * D, a.lpart_ml + row * 2, D, 2, nlong, d0,
-                                   orow);
+                    const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
+                    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, ns, d0, orow);
                 }
             }
         }
@@ -1292,6 +1362,8 @@ void clear_err() { g_err[0] = 0; }
 // per host thread.  Events are reused across begin/end rounds.
 struct Timing {
     bool on = false;
+    int dev = -1;                      // device current at attn_timing_begin
+    unsigned long long* clk = nullptr; // its g_clock, when it could be cleared
     std::vector<std::pair<hipEvent_t, hipEvent_t>> marks;
     std::vector<hipEvent_t> pool;
     hipEvent_t get() {
@@ -1319,6 +1391,14 @@ hipEvent_t timing_start(hipStream_t s) {
     hipEvent_t e = g_timing.get();
     if (e && hipEventRecord(e, s) != hipSuccess) e = nullptr;
     return e;
+}
+
+// Clock sums for a kernel launched now on the current device (null when
+// timing is off or the device is not the one timing began on).
+unsigned long long* timing_clock() {
+    int dev = -1;
+    if (!g_timing.on || !g_timing.clk || hipGetDevice(&dev) != hipSuccess) return nullptr;
+    return dev == g_timing.dev ? g_timing.clk : nullptr;
 }
 
 void timing_stop(hipEvent_t start, hipStream_t s) {
@@ -1418,40 +1498,33 @@ size_t prefill_ws_bytes(int B, int Hq, int Lq, int D, int nsplit) {
     return align256(rows * D * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
-// Key splits of a varlen launch (segments with q_len <= qsplit only):
-// about 256 keys per split over the rows a column can hold.
+// Target keys per split of a varlen q-block (ATTN_VARLEN_SPLIT_KEYS overrides,
+// at least one 64-key tile), and the most splits of a q-block: enough for the
+// longest range a flat column can hold.  A q-block of a longer range (ring
+// storage) takes bigger chunks.
+int varlen_split_keys() {
+    int k = env_int("ATTN_VARLEN_SPLIT_KEYS", kVarlenSplitKeys);
+    return k < kBN ? kBN : k;
+}
+
 int varlen_splits(int rows) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
-    int ns = forced > 0 ? forced : (rows + kShortSplitKeys - 1) / kShortSplitKeys;
+    const int keys = varlen_split_keys();
+    int ns = forced > 0 ? forced : (rows + keys - 1) / keys;
     if (ns < 1) ns = 1;
     if (ns > kMaxVarlenSplits) ns = kMaxVarlenSplits;
     return ns;
 }
 
-// Split bound of the q-blocks of longer segments (no segment sees more than
-// rows keys).
-int varlen_long_splits(int rows) {
-    int forced = env_int("ATTN_FORCE_LONG_SPLITS", 0);
-    int ns = forced > 0 ? forced : (rows + kLongSplitKeys - 1) / kLongSplitKeys;
-    if (ns < 1) ns = 1;
-    if (ns > kMaxLongSplits) ns = kMaxLongSplits;
-    return ns;
-}
-
-// One finish workgroup (and error word) per packed row; one when T == 0.
 int varlen_finish_blocks(int T) { return T > 0 ? T : 1; }
 
 size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
-    RowMap rm = row_map(Hq / Hkv);
-    int qsplit = varlen_qsplit(rm.P);
-    int ns = varlen_splits(rows), nl = varlen_long_splits(rows);
+    (void)S;
+    (void)Hkv;
+    int ns = varlen_splits(rows);
     size_t bytes = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
     if (ns > 1) {
-        size_t prow = (size_t)(S > 0 ? S : 0) * qsplit * Hq * ns;
-        bytes += align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
-    }
-    if (nl > 1) {
-        size_t prow = (size_t)(T > 0 ? T : 0) * Hq * nl;
+        size_t prow = (size_t)(T > 0 ? T : 0) * Hq * ns;
         bytes += align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
     }
     return bytes;
@@ -1549,6 +1622,7 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     a.n_inner = (int)n_inner;
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)nwg);
+    a.clk = timing_clock();
     hipEvent_t t0 = timing_start(s);
     if (D == 64)
         hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
@@ -1621,9 +1695,8 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     DeviceInfo di;
     if ((st = device_info(&di))) return st;
 
-    const int nsplit = varlen_splits(rows), nlong = varlen_long_splits(rows);
+    const int nsplit = varlen_splits(rows);
     RowMap rm = row_map(Hq / Hkv);
-    const int qsplit = varlen_qsplit(rm.P);
     VarlenArgs a;
     a.q = (const u16*)q;
     a.k = (const u16*)k_store;
@@ -1633,20 +1706,11 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.seg_attr = seg_attr;
     a.err = (int32_t*)workspace;
     size_t errb = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
-    size_t prow = (size_t)S * qsplit * Hq * nsplit;
-    char* wp = (char*)workspace + errb;
-    a.part_o = a.part_ml = a.lpart_o = a.lpart_ml = nullptr;
+    a.part_o = a.part_ml = nullptr;
     if (nsplit > 1) {
-        a.part_o = (float*)wp;
-        wp += align256(prow * D * sizeof(float));
-        a.part_ml = (float*)wp;
-        wp += align256(prow * 2 * sizeof(float));
-    }
-    if (nlong > 1) {
-        size_t lrow = (size_t)T * Hq * nlong;
-        a.lpart_o = (float*)wp;
-        wp += align256(lrow * D * sizeof(float));
-        a.lpart_ml = (float*)wp;
+        const size_t prow = (size_t)T * Hq * nsplit;
+        a.part_o = (float*)((char*)workspace + errb);
+        a.part_ml = (float*)((char*)workspace + errb + align256(prow * D * sizeof(float)));
     }
     a.S = S;
     a.T = T;
@@ -1658,7 +1722,7 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.window = window;
     a.ring_rows = ring_rows;
     a.nsplit = nsplit;
-    a.nlong = nlong;
+    a.split_keys = varlen_split_keys();
     // c > 0 keeps exp2(-inf * c) = 0 for masked scores; a zero scale gives
     // weights that round to exactly 1 (uniform)
     a.c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
@@ -1672,12 +1736,15 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
         a.vs[i] = v_str[i];
     }
     hipStream_t s = (hipStream_t)stream;
-    int64_t gx = (int64_t)(T + rm.P - 1) / rm.P + S;
-    int64_t gy = (int64_t)Hkv * rm.hchunks;
-    if (gx > 0x7fffffff || gy > 65535)
-        return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
+    // a bound on the work items of any table: the q-blocks of segments that
+    // share no packed row number at most T / P + S, each with Hkv x hchunks
+    // (kv head, head chunk) pairs and at most nsplit key splits
+    const int64_t gx =
+        ((int64_t)(T + rm.P - 1) / rm.P + S) * ((int64_t)Hkv * rm.hchunks) * nsplit;
+    if (gx > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
     if (gx > 0 && T > 0 && S > 0) {
-        dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)(nsplit > nlong ? nsplit : nlong));
+        dim3 grid((unsigned)gx);
+        a.clk = timing_clock();
         hipEvent_t t0 = timing_start(s);
         if (D == 64)
             hipLaunchKernelGGL(varlen_kernel<64>, grid, dim3(kThreads), 0, s, a);
@@ -1720,6 +1787,17 @@ int attn_timing_begin(void) {
     clear_err();
     g_timing.recycle();
     g_timing.on = true;
+    g_timing.clk = nullptr;
+    g_timing.dev = -1;
+    void* p = nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetSymbolAddress(&p, HIP_SYMBOL(g_clock)) != hipSuccess ||
+        hipMemset(p, 0, sizeof(g_clock)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_OK;  // events still time the kernels; the clock reads as unavailable
+    }
+    g_timing.dev = dev;
+    g_timing.clk = (unsigned long long*)p;
     return ATTN_OK;
 }
 
@@ -1744,6 +1822,32 @@ int attn_timing_end(double* kernel_ms, int* launches) {
     *kernel_ms = total;
     *launches = n;
     return st;
+}
+
+int attn_timing_clock(double* mhz, double xcd_mhz[8]) {
+    clear_err();
+    if (!mhz) return fail(ATTN_ERR_INVALID, "null output pointer");
+    *mhz = 0.0;
+    if (xcd_mhz)
+        for (int i = 0; i < 8; ++i) xcd_mhz[i] = 0.0;
+    if (g_timing.on) return fail(ATTN_ERR_INVALID, "timing is still on (call attn_timing_end first)");
+    if (!g_timing.clk) return fail(ATTN_ERR_HIP, "no clock sums were recorded");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(g_timing.dev) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "could not select the timed device");
+    unsigned long long h[16];
+    hipError_t e = hipMemcpy(h, g_timing.clk, sizeof h, hipMemcpyDeviceToHost);
+    (void)hipSetDevice(cur);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "copy of the clock sums failed");
+    double cyc = 0.0, ref = 0.0;
+    for (int i = 0; i < 8; ++i) {
+        cyc += (double)h[2 * i];
+        ref += (double)h[2 * i + 1];
+        if (xcd_mhz && h[2 * i + 1]) xcd_mhz[i] = 100.0 * (double)h[2 * i] / (double)h[2 * i + 1];
+    }
+    if (ref <= 0.0) return fail(ATTN_ERR_HIP, "no clock sums were recorded");
+    *mhz = 100.0 * cyc / ref;
+    return ATTN_OK;
 }
 
 }  // extern "C"

@@ -154,15 +154,27 @@ int attn_varlen_read_error(const void *workspace, int S, int T, void *stream,
  * Profiling aid (not part of the computation).  After attn_timing_begin(),
  * every attn_causal_prefill / attn_sdpa_varlen call made on the same host
  * thread records a pair of HIP events on its stream around its attention
- * kernel (the split-merge and finish kernels are not included).
- * attn_timing_end() waits for those events, writes the summed kernel time in
- * milliseconds and the number of timed launches, and stops recording.  Events
- * are created on first use and reused; nothing is allocated on the device.
+ * kernel (the split-merge and finish kernels are not included), and the
+ * attention kernels launched on the device that was current at
+ * attn_timing_begin() add their workgroups' lifetimes, in shader cycles and
+ * in the 100 MHz reference clock, to per-XCD sums held in a 128-byte static
+ * device array (no allocation).  attn_timing_begin() clears those sums and
+ * synchronises the device; call it outside graph capture.
+ *
+ * attn_timing_end() waits for the events, writes the summed kernel time in
+ * milliseconds and the number of timed launches, and stops recording.
  * Returns ATTN_ERR_INVALID for null outputs, ATTN_ERR_HIP if an event could
  * not be read (the others are still summed).
+ *
+ * attn_timing_clock(), after attn_timing_end(), writes the average shader
+ * clock in MHz over the timed workgroups (cycles / reference ticks x 100)
+ * and, when xcd_mhz is not NULL, the same per XCD (0 for an XCD that ran
+ * none).  Returns ATTN_ERR_INVALID while timing is on or for a null mhz,
+ * ATTN_ERR_HIP when no sums were recorded or they could not be read.
  */
 int attn_timing_begin(void);
 int attn_timing_end(double *kernel_ms, int *launches);
+int attn_timing_clock(double *mhz, double xcd_mhz[8]);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -159,13 +159,25 @@ def test_oracle_rejects_what_the_library_calls_invalid_varlen(kw):
                       ring_rows=kw.get("ring_rows", 0))
 
 
-def test_varlen_workspace_grows_with_segments_and_rows():
+def test_varlen_workspace_follows_rows_and_packed_rows():
+    """Error words for T rows, then fp32 split partials per packed row: nsplit
+    = min(16, ceil(rows / 512)) splits of (D + 2) floats for each of Hq heads."""
     L = _lib()
+
+    def al(n):
+        return (n + 255) // 256 * 256
+
+    def expect(T, Hq, D, rows):
+        ns = min(16, (rows + 511) // 512)
+        part = al(T * Hq * ns * D * 4) + al(T * Hq * ns * 2 * 4) if ns > 1 else 0
+        return al(max(T, 1) * 4) + part
+
     a = L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 128, 8192, 9)
-    b = L.attn_sdpa_varlen_workspace(16, 1727, 16, 2, 128, 8192, 17)
-    c = L.attn_sdpa_varlen_workspace(8, 4000, 16, 2, 128, 8192, 9)
-    assert 0 < a < b and a < c
-    assert a % 256 == 0
+    assert a == expect(1727, 16, 128, 8192) and a % 256 == 0
+    assert L.attn_sdpa_varlen_workspace(16, 1727, 16, 2, 128, 8192, 17) == a  # not S
+    assert L.attn_sdpa_varlen_workspace(8, 4000, 16, 2, 128, 8192, 9) == expect(4000, 16, 128, 8192)
+    assert L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 64, 3000, 9) == expect(1727, 16, 64, 3000)
+    assert L.attn_sdpa_varlen_workspace(8, 100, 8, 2, 64, 512, 9) == expect(100, 8, 64, 512)
     assert L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 96, 8192, 9) == 0
 
 
@@ -189,3 +201,17 @@ def test_timing_end_rejects_null_outputs_and_counts_nothing_when_idle():
     assert L.attn_timing_end(ctypes.byref(ms), ctypes.byref(n)) == attn.ATTN_OK
     assert ms.value == 0.0 and n.value == 0
     assert L.attn_timing_end(None, ctypes.byref(n)) == attn.ATTN_ERR_INVALID
+
+
+def test_timing_clock_needs_recorded_sums():
+    L = _lib()
+    mhz = ctypes.c_double(-1.0)
+    per = (ctypes.c_double * 8)(*([-1.0] * 8))
+    assert L.attn_timing_clock(None, per) == attn.ATTN_ERR_INVALID
+    assert L.attn_timing_begin() == attn.ATTN_OK
+    assert L.attn_timing_clock(ctypes.byref(mhz), per) == attn.ATTN_ERR_INVALID  # still on
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    assert L.attn_timing_end(ctypes.byref(ms), ctypes.byref(n)) == attn.ATTN_OK
+    # no attention kernel ran, so there are no sums: an error, outputs cleared
+    assert L.attn_timing_clock(ctypes.byref(mhz), per) == attn.ATTN_ERR_HIP
+    assert mhz.value == 0.0 and list(per) == [0.0] * 8

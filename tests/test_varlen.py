@@ -70,12 +70,14 @@ def test_short_query_steps_split_keys(D):
     compare(out, ref, "short steps D%d" % D)
 
 
-@pytest.mark.parametrize("long_splits", [1, 2, 5, 8])
-def test_long_segments_split_keys(long_splits, monkeypatch):
-    """q-blocks of segments longer than a decode step split their visible keys
-    (about 512 a split by default); any split count merges to the oracle."""
-    monkeypatch.setenv("ATTN_FORCE_LONG_SPLITS", str(long_splits))
-    say("varlen long splits", long_splits)
+@pytest.mark.parametrize("split_keys,cap", [(64, None), (200, None), (64, 3), (100000, None)])
+def test_split_sizes_match_oracle(split_keys, cap, monkeypatch):
+    """Every q-block splits its visible keys into chunks of about split_keys
+    (at most 16, or the cap); any split size merges to the oracle."""
+    monkeypatch.setenv("ATTN_VARLEN_SPLIT_KEYS", str(split_keys))
+    if cap is not None:
+        monkeypatch.setenv("ATTN_FORCE_SPLITS", str(cap))
+    say("varlen split keys", split_keys, "cap", cap)
     st = synth.VARLEN_STORE
     info, attr, T = synth.pinned_varlen_table()
     q, ks, vs = synth.varlen_inputs(T, st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"],
@@ -83,7 +85,7 @@ def test_long_segments_split_keys(long_splits, monkeypatch):
     out, err = _gpu_varlen(q, ks, vs, info, attr)
     ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
     assert err == 0
-    compare(out, ref, "long splits %d" % long_splits)
+    compare(out, ref, "split keys %d cap %s" % (split_keys, cap))
 
 
 @pytest.mark.parametrize("D", [64, 128])
