@@ -1162,22 +1162,34 @@ __device__ inline void block_range(const Segment& g, int qb, int P, int64_t* lo,
 // key by which items are ordered longest first.  The largest key range of a
 // segment's q-blocks is its first or its last one's (the range size is
 // monotone in the block index in every mode).
+//
+// A segment whose rows (q_len positions x the gq query heads of a kv head)
+// fit one 32-row tile is planned as decode items instead: one per (kv head,
+// split), its whole q_len in one block (see decode_item).  Their cost counts
+// the 64-key tiles of one wave, plus one for the latency of the first.
 struct SegPlan {
     int nqb, nsplit, cost, count;
+    bool decode;
 };
 
-__device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int split_keys, int nsplit_max) {
-    SegPlan p{0, 1, 0, 0};
+__device__ inline bool decode_rows(int gq, int q_len) { return gq * q_len <= 32; }
+
+__device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int gq, int hkv, int split_keys,
+                                   int nsplit_max) {
+    SegPlan p{0, 1, 0, 0, false};
     if (g.flags || g.q_len <= 0) return p;
-    p.nqb = (g.q_len + P - 1) / P;
+    p.decode = decode_rows(gq, g.q_len);
+    const int Pb = p.decode ? g.q_len : P;  // positions per q-block
+    p.nqb = (g.q_len + Pb - 1) / Pb;
     int64_t lo, hi, pmn, pmx, lo1, hi1;
-    block_range(g, 0, P, &lo, &hi, &pmn, &pmx);
-    block_range(g, p.nqb - 1, P, &lo1, &hi1, &pmn, &pmx);
+    block_range(g, 0, Pb, &lo, &hi, &pmn, &pmx);
+    block_range(g, p.nqb - 1, Pb, &lo1, &hi1, &pmn, &pmx);
     const int64_t span = max(hi - lo, hi1 - lo1);
     const int64_t n = (span + split_keys - 1) / split_keys;
     p.nsplit = n < 1 ? 1 : (n > nsplit_max ? nsplit_max : (int)n);
-    p.cost = (int)min((int64_t)0x3fffffff, ((span + p.nsplit - 1) / p.nsplit + kBN - 1) / kBN);
-    p.count = p.nqb * hg * p.nsplit;
+    const int64_t tiles = ((span + p.nsplit - 1) / p.nsplit + kBN - 1) / kBN;
+    p.cost = (int)min((int64_t)0x3fffffff, p.decode ? (tiles + kWaves - 1) / kWaves + 1 : tiles);
+    p.count = p.decode ? hkv * p.nsplit : p.nqb * hg * p.nsplit;
     return p;
 }
 
@@ -1187,22 +1199,25 @@ __device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int split_ke
 // schedules longest items first.  Each thread plans its own segments, then
 // sums the item counts of the segments ordered before them; one thread finds
 // the segment that holds L.  Returns false when L is past the last item.
-__device__ bool pick_item(const VarlenArgs& a, int P, int hg, int L, int* seg_out, int* j_out) {
+__device__ bool pick_item(const VarlenArgs& a, int P, int hg, int gq, int L, int* seg_out,
+                          int* j_out) {
     constexpr int NT = kThreads;  // one segment per thread per pass
     __shared__ int sh_cost[NT], sh_count[NT];
     __shared__ int sh_seg, sh_j;
     if (threadIdx.x == 0) sh_seg = -1;
     for (int c0 = 0; c0 < a.S; c0 += NT) {
         const int s = c0 + threadIdx.x;
-        const SegPlan ps = s < a.S ? seg_plan(read_segment(a, s), P, hg, a.split_keys, a.nsplit)
-                                   : SegPlan{0, 1, 0, 0};
+        const SegPlan ps = s < a.S ? seg_plan(read_segment(a, s), P, hg, gq, a.Hkv, a.split_keys,
+                                              a.nsplit)
+                                   : SegPlan{0, 1, 0, 0, false};
         int64_t off = 0;
         for (int d0 = 0; d0 < a.S; d0 += NT) {
             const int s2 = d0 + threadIdx.x;
             SegPlan p2 = ps;
             if (d0 != c0)
-                p2 = s2 < a.S ? seg_plan(read_segment(a, s2), P, hg, a.split_keys, a.nsplit)
-                              : SegPlan{0, 1, 0, 0};
+                p2 = s2 < a.S ? seg_plan(read_segment(a, s2), P, hg, gq, a.Hkv, a.split_keys,
+                                         a.nsplit)
+                              : SegPlan{0, 1, 0, 0, false};
             __syncthreads();
             sh_cost[threadIdx.x] = p2.cost;
             sh_count[threadIdx.x] = p2.count;
@@ -1224,6 +1239,176 @@ __device__ bool pick_item(const VarlenArgs& a, int P, int hg, int L, int* seg_ou
     return sh_seg >= 0;
 }
 
+// ---------------------------------------------------------------- decode items
+//
+// Few rows and many keys: such an item is bound by the K/V stream, so every
+// wave streams its own key tiles instead of sharing one pipeline.  Wave w
+// takes the 64-key tiles w, w + 8, ... of the split's range, each with the
+// item's (at most 32) rows: K straight into the MFMA operand registers, V
+// into the wave's own LDS tile (the transposing reads need it there), then
+// the exact online softmax.  With one tile in flight per wave, a workgroup
+// keeps eight tiles of loads outstanding.  The eight states then merge
+// through LDS into one partial (or the output when the range is not split).
+
+// K operand registers of one 64-key tile: lane l holds key k0 + 32t + l%32,
+// d = 16kk + 8(l/32) .. +8 (the layout k_frag reads from LDS).  Keys at or
+// past k_hi repeat key k_hi - 1 (their scores are masked).
+template <int D>
+__device__ inline void load_k_regs(bf16x8 (&kr)[2][D / 16], const KVRing& kv, int k0, int k_hi) {
+    const int lane = threadIdx.x & (kWave - 1), hh = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int k = min(k0 + 32 * t + (lane & 31), k_hi - 1);
+        const u16* row = kv.krow_at((int)((unsigned)k % (unsigned)kv.R));
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            kr[t][kk] = __builtin_bit_cast(bf16x8, ld16(row + 16 * kk + 8 * hh));
+    }
+}
+
+// This wave alone copies V rows [k0, k0 + 64) into its LDS tile (the layout
+// of the workgroup copies: instruction i fills rows i*ROWS.., chunk c of row
+// r at position c ^ swz(r)); rows at or past k_hi repeat row k_hi - 1.
+template <int D>
+__device__ inline void copy_v_wave(const KVRing& kv, int k0, int k_hi, u16* dst) {
+    constexpr int CH = D / 8, ROWS = 64 / CH, INSTR = kBN / ROWS;
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+        const int r = i * ROWS + lane / CH;
+        const int k = min(k0 + r, k_hi - 1);
+        const int row = (int)((unsigned)k % (unsigned)kv.R);
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(kv.vb + (int64_t)row * kv.vs + 8 * ((lane % CH) ^ swz<D>(r))),
+            (lds_void*)(dst + i * 512), 16, 0, 0);
+    }
+}
+
+// The eight waves' 64-key V tiles of a decode item (the merge reuses them as
+// fp32 buffers of the waves' accumulators).  Indexed with constants only.
+struct WaveBufs {
+    u16* b[kWaves];
+};
+
+// One decode item: kv head hk, split `split` of nsplit of the segment's
+// visible keys, all q_len positions x gq heads as rows r = hl * q_len + pos.
+template <int D>
+__device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& sg, int hk,
+                                            int split, int nsplit, WaveBufs wb) {
+    constexpr int NREG = (D / 32) * 16;  // accumulator floats per lane
+    constexpr int RPW = NREG / kWaves;   // of which each wave merges
+    __shared__ float sh_m[kWaves][32], sh_l[kWaves][32];
+    const int gq = a.Hq / a.Hkv;
+    const int lane = threadIdx.x & (kWave - 1), hh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    u16* vbuf = wb.b[0];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) vbuf = w == v ? wb.b[v] : vbuf;
+    const int r = lane & 31, hl = r / sg.q_len, pos = r % sg.q_len;
+    const bool valid = r < gq * sg.q_len;
+    const int t = sg.q_start + pos, h = hk * gq + hl;
+    const int64_t base = (int64_t)sg.kv_end - sg.q_len;
+    int64_t lo64, hi64, p_min, p_max;
+    block_range(sg, 0, sg.q_len, &lo64, &hi64, &p_min, &p_max);
+    const int64_t p_lane = valid ? base + pos : p_max;
+    int k_lo, k_hi;
+    split_range((int)lo64, (int)hi64, split, nsplit, &k_lo, &k_hi);
+
+    bf16x8 qf[1][D / 16];
+    load_q<D>(qf[0], a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid, a.negate);
+    const KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
+                    a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0],
+                    sg.R};
+    const LaneBounds lb = lane_bounds(k_lo, k_hi, sg.causal, sg.window, p_lane);
+    RowState<D> st;
+    init_state<D>(st);
+    const int n = (k_hi - k_lo + kBN - 1) / kBN;
+    for (int tile = w; tile < n; tile += kWaves) {
+        const int k0 = k_lo + tile * kBN;
+        copy_v_wave<D>(kv, k0, k_hi, vbuf);
+        bf16x8 kr[2][D / 16];
+        load_k_regs<D>(kr, kv, k0, k_hi);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K registers and the V tile
+        TileScores S;
+        S[0][0] = S[0][1] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            S[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[0][kk], qf[0][kk], S[0][0], 0, 0, 0);
+            S[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[1][kk], qf[0][kk], S[0][1], 0, 0, 0);
+        }
+        mask_tile(S, k0, &lb);
+        float alpha[1], lsum[1];
+        update_max(S, a.c, st.m, alpha);
+        rescale<D>(alpha, st);
+        TileP pk;
+        softmax_tile(S, a.c, st.m, pk, lsum);
+        st.l[0] += lsum[0];
+        pv_tile<D>(vbuf, pk, st, NoCopy{});
+    }
+
+    // merge: M = max of the waves' maxima, each wave's share scaled by
+    // 2^((m_w - M) c), then summed over the waves element by element
+    const float lw = sum_across_halves(st.l[0]);
+    if (lane < 32) {
+        sh_m[w][lane] = st.m[0];
+        sh_l[w][lane] = lw;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = __builtin_fmaxf(M, sh_m[v][r]);
+    const float mref = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float mv = sh_m[v][r];
+        L += mv == -INFINITY ? 0.f : sh_l[v][r] * __builtin_amdgcn_exp2f((mv - mref) * a.c);
+    }
+    const float fw = st.m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[0] - mref) * a.c);
+    float* ob = reinterpret_cast<float*>(vbuf);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ob[(dt * 16 + i) * kWave + lane] = st.o[0][dt][i] * fw;
+    __syncthreads();
+    float acc[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const float* obv = reinterpret_cast<const float*>(wb.b[v]);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) acc[j] += obv[(w * RPW + j) * kWave + lane];
+    }
+    if (!valid) return;
+    // register ri = dt*16 + i of a lane holds d = 32dt + 8(i/4) + 4hh + i%4
+    if (nsplit == 1) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
+#pragma unroll
+        for (int j = 0; j < RPW; j += 4) {
+            const int ri = w * RPW + j, dt = ri / 16, i = ri % 16;
+            const int d = 32 * dt + 8 * (i / 4) + 4 * hh;
+            *reinterpret_cast<uint2*>(orow + d) =
+                make_uint2(pack_bf16x2(acc[j] * inv, acc[j + 1] * inv),
+                           pack_bf16x2(acc[j + 2] * inv, acc[j + 3] * inv));
+        }
+    } else {
+        const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit + split;
+        float* po = a.part_o + row * D;
+#pragma unroll
+        for (int j = 0; j < RPW; j += 4) {
+            const int ri = w * RPW + j, dt = ri / 16, i = ri % 16;
+            const int d = 32 * dt + 8 * (i / 4) + 4 * hh;
+            *reinterpret_cast<float4*>(po + d) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        }
+        if (w == 0 && hh == 0) {
+            a.part_ml[row * 2] = L > 0.f ? mref * a.c : -INFINITY;
+            a.part_ml[row * 2 + 1] = L;
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     DECLARE_TILE_SMEM(D);
@@ -1235,9 +1420,24 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 
     // this workgroup's work item: (segment, item j of that segment)
     int seg, j;
-    if (!pick_item(a, rm.P, hg, blockIdx.x, &seg, &j)) return;
+    if (!pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j)) return;
     const Segment sg = read_segment(a, seg);
-    const SegPlan pl = seg_plan(sg, rm.P, hg, a.split_keys, a.nsplit);
+    const SegPlan pl = seg_plan(sg, rm.P, hg, g, a.Hkv, a.split_keys, a.nsplit);
+    if (pl.decode) {
+        __shared__ __attribute__((aligned(1024))) u16 sx[2 * kBN * D];
+        WaveBufs wb;
+        wb.b[0] = sk0;
+        wb.b[1] = sv0;
+        wb.b[2] = sk1;
+        wb.b[3] = sv1;
+        wb.b[4] = sk2;
+        wb.b[5] = sv2;
+        wb.b[6] = sx;
+        wb.b[7] = sx + kBN * D;
+        decode_item<D>(a, sg, j % a.Hkv, j / a.Hkv, pl.nsplit, wb);
+        clock_add(a.clk, cm);
+        return;
+    }
     // item j: q-blocks from the last (the longest under causal masking),
     // then split, then (kv head, head chunk)
     const int per_qb = hg * pl.nsplit;
@@ -1323,7 +1523,8 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
         const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
         int ns = 1;
         if (owner >= 0)
-            ns = seg_plan(read_segment(a, owner), rm.P, a.Hkv * rm.hchunks, a.split_keys, a.nsplit)
+            ns = seg_plan(read_segment(a, owner), rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys,
+                          a.nsplit)
                      .nsplit;
         if (owner < 0 || ns > 1) {
             constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
