@@ -6,7 +6,9 @@ from ``oracle.c`` by ``oracle/build.py``) and marshals torch CPU tensors into
 it.  It never touches a GPU and imports nothing from the HIP library.
 
 What the C code computes, and which passages of the pages it follows, is
-stated in the header of ``oracle.c``.
+stated in the header of ``oracle.c``.  ``kv_write`` (the step's K/V slot
+write before the varlen attention) is plain data movement and is written
+here directly, a Python loop over the step's tokens.
 """
 import ctypes
 import os
@@ -24,6 +26,11 @@ SEGF_COL = 2
 SEGF_KVEND = 4
 SEGF_ATTR = 8
 SEGF_OVERLAP = 16
+
+# Bit meanings of the slot-write token flags.
+KVF_COL = 1
+KVF_POS = 2
+KVF_ROWS = 4
 
 
 class OracleInvalid(ValueError):
@@ -151,3 +158,54 @@ def varlen(q, k_store, v_store, seq_info, T=None, seg_attr=None, scale=None,
     if return_flags:
         return torch.from_numpy(out), int(err[0])
     return torch.from_numpy(out)
+
+
+def kv_write(k_store, v_store, k_new, v_new, positions, seq_cols, slot_rows=None):
+    """The K/V slot write of one step (the plain definition), functional.
+
+    Follows "[executorch][cuda] Add a length-aware Triton SDPA over
+    per-sequence KV columns", the stacked commits on the batched-sequence
+    manifest layout (each step token is written to slot (position mod rows)
+    x columns + its column, i.e. store row position mod R of that column)
+    and on the batched sequence cache (one column per sequence, the last
+    column scratch for padded writes; a ring layer's row count is its
+    modulus).
+
+    k_store/v_store [rows, cols, Hkv, D] and k_new/v_new [T, Hkv, D]: CPU
+    bf16.  positions int64 [T], seq_cols int32 [T]; slot_rows optional int32
+    [T], the modulus R of each token (<= 0: rows).  Token i writes
+    new[i, h, :] to store[positions[i] mod R_i, seq_cols[i], h, :].  A token
+    with a column outside [0, cols), a negative position or R_i > rows is
+    skipped and flagged (KVF_COL, KVF_POS, KVF_ROWS).  Tokens are applied in
+    order, so when two share a slot the later one stays.
+    Returns (k_out, v_out, OR of the flags).
+    """
+    rows, cols, Hkv, D = k_store.shape
+    T = k_new.shape[0]
+    if tuple(v_store.shape) != tuple(k_store.shape) or tuple(k_new.shape) != (T, Hkv, D) \
+            or tuple(v_new.shape) != (T, Hkv, D):
+        raise OracleInvalid("shape mismatch")
+    pos = [int(x) for x in positions]
+    col = [int(x) for x in seq_cols]
+    rr = [int(x) for x in slot_rows] if slot_rows is not None else [0] * T
+    if len(pos) != T or len(col) != T or len(rr) != T:
+        raise OracleInvalid("per-token arrays must have T entries")
+    k_out = k_store.clone()
+    v_out = v_store.clone()
+    flags = 0
+    for i in range(T):
+        R = rows if rr[i] <= 0 else rr[i]
+        f = 0
+        if not 0 <= col[i] < cols:
+            f |= KVF_COL
+        if pos[i] < 0:
+            f |= KVF_POS
+        if R > rows:
+            f |= KVF_ROWS
+        flags |= f
+        if f:
+            continue
+        r = pos[i] % R
+        k_out[r, col[i]] = k_new[i]
+        v_out[r, col[i]] = v_new[i]
+    return k_out, v_out, flags

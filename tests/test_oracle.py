@@ -420,3 +420,101 @@ def test_varlen_invalid_segments_are_flagged_and_skipped():
         oracle.varlen(q, ks, vs, [(0, 4, 0, 8), (3, 2, 1, 6)], scale=0.3)
     with pytest.raises(oracle.OracleInvalid):  # more segments than 2 x (cols - 1)
         oracle.varlen(q, ks, vs, [(i, 1, 0, 4) for i in range(5)], scale=0.3)
+
+
+# ------------------------------------------------------------------ slot write
+
+def _kv_step(T, rows, cols, Hkv, D, wid):
+    ks = synth.randn_bf16((rows, cols, Hkv, D), 9000 + wid)
+    vs = synth.randn_bf16((rows, cols, Hkv, D), 9100 + wid)
+    kn = synth.randn_bf16((T, Hkv, D), 9200 + wid)
+    vn = synth.randn_bf16((T, Hkv, D), 9300 + wid)
+    return ks, vs, kn, vn
+
+
+def test_kv_write_matches_index_copy_on_the_flattened_slots():
+    """Distinct slots: the write is index_copy_ over the [rows*cols] slot axis
+    with slot = (position mod rows) * cols + column."""
+    rows, cols, Hkv, D = 40, 5, 2, 16
+    ks, vs, kn, vn = _kv_step(12, rows, cols, Hkv, D, 1)
+    pos = torch.tensor([0, 1, 2, 39, 40, 41, 7, 80, 5, 6, 119, 3], dtype=torch.int64)
+    col = torch.tensor([0, 0, 0, 1, 1, 1, 2, 2, 3, 3, 4, 4], dtype=torch.int32)
+    k2, v2, f = oracle.kv_write(ks, vs, kn, vn, pos, col)
+    assert f == 0
+    slots = (pos % rows) * cols + col.to(torch.int64)
+    assert len(set(slots.tolist())) == len(slots)
+    kr = ks.clone().view(rows * cols, Hkv, D).index_copy_(0, slots, kn).view_as(ks)
+    vr = vs.clone().view(rows * cols, Hkv, D).index_copy_(0, slots, vn).view_as(vs)
+    assert torch.equal(k2.view(torch.int16), kr.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), vr.view(torch.int16))
+
+
+def test_kv_write_ring_modulus_and_untouched_slots():
+    """Per-token ring rows: position p lands at row p mod R; every other slot
+    keeps its bits; gathering the written slots returns the new rows."""
+    rows, cols, Hkv, D = 32, 4, 1, 8
+    ks, vs, kn, vn = _kv_step(6, rows, cols, Hkv, D, 2)
+    pos = torch.tensor([10, 11, 12, 25, 26, 31], dtype=torch.int64)
+    col = torch.tensor([1, 1, 1, 2, 2, 3], dtype=torch.int32)
+    R = torch.tensor([7, 7, 7, 0, 0, 32], dtype=torch.int32)
+    k2, v2, f = oracle.kv_write(ks, vs, kn, vn, pos, col, slot_rows=R)
+    assert f == 0
+    expect_rows = [3, 4, 5, 25, 26, 31]
+    touched = set()
+    for i, r in enumerate(expect_rows):
+        assert torch.equal(k2[r, col[i]], kn[i]) and torch.equal(v2[r, col[i]], vn[i])
+        touched.add((r, int(col[i])))
+    for r in range(rows):
+        for c in range(cols):
+            if (r, c) not in touched:
+                assert torch.equal(k2[r, c], ks[r, c]) and torch.equal(v2[r, c], vs[r, c])
+
+
+def test_kv_write_flags_and_skips_invalid_tokens():
+    rows, cols, Hkv, D = 16, 3, 1, 8
+    ks, vs, kn, vn = _kv_step(4, rows, cols, Hkv, D, 3)
+    pos = torch.tensor([1, -1, 2, 3], dtype=torch.int64)
+    col = torch.tensor([3, 0, -1, 1], dtype=torch.int32)
+    R = torch.tensor([0, 0, 0, 17], dtype=torch.int32)
+    k2, v2, f = oracle.kv_write(ks, vs, kn, vn, pos, col, slot_rows=R)
+    assert f == oracle.KVF_COL | oracle.KVF_POS | oracle.KVF_ROWS
+    assert torch.equal(k2.view(torch.int16), ks.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), vs.view(torch.int16))
+
+
+def test_kv_write_later_token_wins_a_shared_slot():
+    rows, cols, Hkv, D = 8, 2, 1, 8
+    ks, vs, kn, vn = _kv_step(3, rows, cols, Hkv, D, 4)
+    pos = torch.tensor([2, 10, 18], dtype=torch.int64)   # all row 2
+    col = torch.tensor([1, 1, 1], dtype=torch.int32)
+    k2, v2, _ = oracle.kv_write(ks, vs, kn, vn, pos, col)
+    assert torch.equal(k2[2, 1], kn[2]) and torch.equal(v2[2, 1], vn[2])
+
+
+def test_kv_write_then_attend_reads_the_written_key():
+    """Write convention = read convention: after a step writes position p of
+    a sequence, a one-query segment that sees only key p (window 1) returns
+    exactly the written V row, and a segment ending at p + 1 attends over the
+    written key with the stored ones."""
+    rows, cols, Hkv, D, Hq = 24, 3, 2, 16, 4
+    ks, vs, kn, vn = _kv_step(2, rows, cols, Hkv, D, 5)
+    R = 10
+    pos = torch.tensor([23, 23], dtype=torch.int64)       # row 3 of a 10-row ring
+    col = torch.tensor([0, 1], dtype=torch.int32)
+    k2, v2, f = oracle.kv_write(ks, vs, kn, vn, pos, col,
+                                slot_rows=torch.tensor([R, 0], dtype=torch.int32))
+    assert f == 0
+    q = synth.randn_bf16((2, Hq, D), 9400)
+    info = torch.tensor([(0, 1, 0, 24), (1, 1, 1, 24)], dtype=torch.int32)
+    attr = torch.tensor([(1, 1, R), (1, 1, 0)], dtype=torch.int32)   # window 1: only key 23
+    out = oracle.varlen(q, k2, v2, info, seg_attr=attr)
+    g = Hq // Hkv
+    for t in range(2):
+        for h in range(Hq):
+            assert torch.equal(out[t, h], vn[t, h // g].double())
+    # a plain causal segment sees the new key at its own position as well
+    full = oracle.varlen(q[:1], k2, v2, info[:1], seg_attr=torch.tensor([(1, 0, R)],
+                                                                     dtype=torch.int32))
+    stale = oracle.varlen(q[:1], ks, vs, info[:1], seg_attr=torch.tensor([(1, 0, R)],
+                                                                      dtype=torch.int32))
+    assert not torch.allclose(full, stale)
