@@ -18,6 +18,8 @@ workload on the host cores.  Varlen workloads (--workload varlen_pinned,
 varlen_short) report HBM GB/s of algorithmic bytes instead; their step time
 comes from replaying a captured graph of 10 back-to-back launches that
 rotate over 8 copies of the store (more than the last-level cache holds).
+--workload kv_write_pinned times the step's K/V slot write alone (GB/s) and
+step_pinned the slot write followed by the varlen attention (us per step).
 
 The roofline object also carries the average shader clock the timed
 attention workgroups ran at (per XCD too) and, for the MFMA peak, the
@@ -342,6 +344,88 @@ def bench_varlen(args, name):
     }
 
 
+def bench_kv_write(args, name):
+    """The step's K/V slot write (kv_write_pinned: the pinned table's step
+    tokens into the column store), alone and followed by the varlen attention
+    as one step (step_pinned); both replayed from captured graphs of 10
+    launches rotating over 8 store copies."""
+    import causal_gqa_prefill_flash_amd as attn
+    from causal_gqa_prefill_flash_amd import synth
+    st = synth.VARLEN_STORE
+    rows, cols, Hkv, D, Hq = st["rows"], st["cols"], st["Hkv"], st["D"], st["Hq"]
+    info, attr, T = synth.pinned_varlen_table()
+    pos, col, srows = [], [], []
+    for s_ in range(info.shape[0]):
+        q_start, q_len, c, kv_end = (int(x) for x in info[s_])
+        for j in range(q_len):
+            pos.append(kv_end - q_len + j)
+            col.append(c)
+            srows.append(int(attr[s_][2]))
+    n = len(pos)
+    dev = torch.device("cuda:0")
+    posd = torch.tensor(pos, dtype=torch.int64, device=dev)
+    cold = torch.tensor(col, dtype=torch.int32, device=dev)
+    srd = torch.tensor(srows, dtype=torch.int32, device=dev)
+    kn = synth.randn_bf16((n, Hkv, D), 7200).to(dev)
+    vn = synth.randn_bf16((n, Hkv, D), 7201).to(dev)
+    q = synth.varlen_inputs(T, 8, cols, Hkv, D, Hq, wid=60)[0].to(dev)
+    ncopy = 8
+    stores = [(synth.randn_bf16((rows, cols, Hkv, D), 7000 + c).to(dev),
+               synth.randn_bf16((rows, cols, Hkv, D), 7100 + c).to(dev)) for c in range(ncopy)]
+    si, sa = info.to(dev), attr.to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    kws = torch.empty(attn.kv_write_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    vws = torch.empty(attn.varlen_workspace_bytes(len(info), T, Hq, Hkv, D, rows, cols),
+                      dtype=torch.uint8, device=dev)
+    with_attend = name == "step_pinned"
+
+    def launch(c):
+        ks, vs = stores[c % ncopy]
+
+        def f():
+            attn.kv_write(kn, vn, ks, vs, posd, cold, srd, workspace=kws)
+            if with_attend:
+                attn.sdpa_varlen(q, ks, vs, si, seg_attr=sa, out=out, workspace=vws)
+        return f
+
+    ms = time_graph([launch(c) for c in range(10)], args.steps, args.warmup)
+    assert attn.kv_write_read_error(kws, n) == 0
+    wbytes = n * Hkv * D * 2 * 2 * 2  # K and V rows: read once, written once
+    if with_attend:
+        pairs, kv_rows = varlen_pairs_and_bytes(info, attr, Hq, Hkv, D)
+        abytes = kv_rows * Hkv * D * 2 * 2 + T * Hq * D * 2 * 2
+        return {
+            "metric": "decode/prefill step time (slot write + varlen SDPA)",
+            "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "timed": "graph replay: one captured graph of 10 steps (slot write + attention), "
+                     "each on the next of %d store copies; ms_per_step = graph time / 10" % ncopy,
+            "config": {"workload": name, "rows": rows, "cols": cols, "Hkv": Hkv, "D": D,
+                       "Hq": Hq, "T": T, "S": int(info.shape[0]), "step_tokens": n,
+                       "store_copies_rotated": ncopy},
+            "roofline": {"bound": "hbm", "achieved": round((wbytes + abytes) / (ms * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round((wbytes + abytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": wbytes + abytes},
+        }
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "KV slot write HBM GB/s (algorithmic bytes)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "timed": "graph replay: one captured graph of 10 launches, each on the next of %d "
+                 "store copies; ms_per_step = graph time / 10" % ncopy,
+        "config": {"workload": name, "rows": rows, "cols": cols, "Hkv": Hkv, "D": D,
+                   "step_tokens": n, "store_copies_rotated": ncopy},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": wbytes,
+                     "kernel": "kv_write_kernel"},
+    }
+
+
 def calibrate_copy():
     """A plain device copy of known size (256 MiB read, 256 MiB written),
     three times, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -379,6 +463,8 @@ def main():
         return
     if args.workload.startswith("varlen"):
         line = bench_varlen(args, args.workload)
+    elif args.workload in ("kv_write_pinned", "step_pinned"):
+        line = bench_kv_write(args, args.workload)
     else:
         line = bench_prefill(args, args.workload)
     print(json.dumps(line), flush=True)

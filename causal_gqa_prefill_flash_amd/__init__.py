@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP = 1, 2, 4, 8, 16
+KV_COL, KV_POS, KV_ROWS = 1, 2, 4
 
 
 class AttnError(RuntimeError):
@@ -54,6 +55,13 @@ def lib():
                                    I, I, I, I64A, I64A, I64A, I64A, P, SZ, P]
     L.attn_varlen_read_error.restype = I
     L.attn_varlen_read_error.argtypes = [P, I, I, P, ctypes.POINTER(ctypes.c_int32)]
+    L.attn_kv_write_workspace.restype = SZ
+    L.attn_kv_write_workspace.argtypes = [I]
+    L.attn_kv_write.restype = I
+    L.attn_kv_write.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I64A, I64A, I64A, I64A,
+                                P, SZ, P]
+    L.attn_kv_write_read_error.restype = I
+    L.attn_kv_write_read_error.argtypes = [P, I, P, ctypes.POINTER(ctypes.c_int32)]
     L.attn_timing_begin.restype = I
     L.attn_timing_begin.argtypes = []
     L.attn_timing_end.restype = I
@@ -219,3 +227,46 @@ def timing_clock():
     mhz, per = ctypes.c_double(0.0), (ctypes.c_double * 8)()
     _check(lib().attn_timing_clock(ctypes.byref(mhz), per))
     return mhz.value, list(per)
+
+
+def kv_write_workspace_bytes(T):
+    return lib().attn_kv_write_workspace(T)
+
+
+def kv_write(k_new, v_new, k_store, v_store, positions, seq_cols, slot_rows=None,
+             workspace=None):
+    """Write a step's new K/V rows [T,Hkv,D] into the [rows,cols,Hkv,D] stores
+    at row positions[i] mod R_i of column seq_cols[i] (R_i = slot_rows[i],
+    else rows).  positions int64 [T], seq_cols / slot_rows int32 [T], device
+    tensors.  Returns the workspace that holds the error word (read it with
+    ``kv_write_read_error``)."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_store, "k_store"), (v_store, "v_store")):
+        _gpu(t, n)
+    T, Hkv, D = k_new.shape
+    rows, cols, Hs, Ds = k_store.shape
+    if (Hs, Ds) != (Hkv, D) or tuple(v_new.shape) != (T, Hkv, D) or \
+            tuple(v_store.shape) != tuple(k_store.shape):
+        raise ValueError("new-row and store shapes do not agree")
+    for t, n, dt in ((positions, "positions", torch.int64), (seq_cols, "seq_cols", torch.int32),
+                     (slot_rows, "slot_rows", torch.int32)):
+        if t is None:
+            continue
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous() or t.numel() != T:
+            raise ValueError("%s must be a contiguous %s device tensor of %d entries" % (n, dt, T))
+    with torch.cuda.device(k_store.device):
+        need = kv_write_workspace_bytes(T)
+        ws = _workspace(need, k_store.device, workspace)
+        st = lib().attn_kv_write(
+            _ptr(k_new), _ptr(v_new), _ptr(k_store), _ptr(v_store), _ptr(positions),
+            _ptr(seq_cols), _ptr(slot_rows), T, Hkv, D, rows, cols, _strides(k_new, 3),
+            _strides(v_new, 3), _strides(k_store, 4), _strides(v_store, 4), _ptr(ws), need,
+            _stream())
+    _check(st)
+    return ws
+
+
+def kv_write_read_error(workspace, T):
+    """OR of the ATTN_KV_* flags of the last kv_write call on ``workspace``."""
+    e = ctypes.c_int32(0)
+    _check(lib().attn_kv_write_read_error(_ptr(workspace), T, _stream(), ctypes.byref(e)))
+    return e.value

@@ -1543,6 +1543,64 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh | (count_sh > 1 ? ATTN_SEG_OVERLAP : 0);
 }
 
+// ---------------------------------------------------------------- slot write
+//
+// The step's new K/V rows go to row position mod R of their sequence's
+// column ("[executorch][cuda] Add a length-aware Triton SDPA over
+// per-sequence KV columns": the batched-sequence manifest layout writes slot
+// (position mod rows) x columns + column; the batched sequence cache gives
+// each sequence a column, a scratch last column, and ring layers of R rows).
+// One wave per token copies its Hkv x D values of K and of V in 16-byte
+// pieces; four tokens per workgroup, whose flags form its error word.
+
+struct KVWriteArgs {
+    const u16* kn;
+    const u16* vn;
+    u16* ks;
+    u16* vs;
+    const int64_t* pos;
+    const int32_t* col;
+    const int32_t* srows;  // per-token modulus (<= 0: rows), or null
+    int32_t* err;          // one word per workgroup
+    int T, Hkv, D, rows, cols;
+    int64_t kns[3], vns[3], kss[4], vss[4];
+};
+
+constexpr int kWriteTokens = 4;  // tokens (waves) per slot-write workgroup
+
+__global__ __launch_bounds__(kWriteTokens * kWave) void kv_write_kernel(KVWriteArgs a) {
+    __shared__ int flags_sh;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = blockIdx.x * kWriteTokens + (int)(threadIdx.x / kWave);
+    if (threadIdx.x == 0) flags_sh = 0;
+    __syncthreads();
+    int f = 0;
+    if (i < a.T) {
+        const int64_t p = a.pos[i];
+        const int c = a.col[i];
+        const int rr = a.srows ? a.srows[i] : 0;
+        const int R = rr > 0 ? rr : a.rows;
+        if (c < 0 || c >= a.cols) f |= ATTN_KV_COL;
+        if (p < 0) f |= ATTN_KV_POS;
+        if (R > a.rows) f |= ATTN_KV_ROWS;
+        if (!f) {
+            const int64_t r = p % R;
+            const int per_head = a.D / 8;  // 16-byte pieces of one head's row
+            for (int e = lane; e < a.Hkv * per_head; e += kWave) {
+                const int h = e / per_head, d = (e % per_head) * 8;
+                const uint4 kx = ld16(a.kn + i * a.kns[0] + h * a.kns[1] + d);
+                const uint4 vx = ld16(a.vn + i * a.vns[0] + h * a.vns[1] + d);
+                *reinterpret_cast<uint4*>(a.ks + r * a.kss[0] + c * a.kss[1] + h * a.kss[2] + d) = kx;
+                *reinterpret_cast<uint4*>(a.vs + r * a.vss[0] + c * a.vss[1] + h * a.vss[2] + d) = vx;
+            }
+        } else if (lane == 0) {
+            atomicOr(&flags_sh, f);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh;
+}
+
 // ---------------------------------------------------------------- host side
 
 thread_local char g_err[512];
@@ -1980,6 +2038,91 @@ int attn_varlen_read_error(const void* workspace, int S, int T, void* stream, in
     int32_t e = 0;
     for (int i = 0; i < n; ++i) e |= host[i];
     free(host);
+    *err_out = e;
+    return ATTN_OK;
+}
+
+int kv_write_blocks(int T) { return T > 0 ? (T + kWriteTokens - 1) / kWriteTokens : 0; }
+
+size_t attn_kv_write_workspace(int T) {
+    if (T < 0) return 0;
+    return align256((size_t)(kv_write_blocks(T) > 0 ? kv_write_blocks(T) : 1) * sizeof(int32_t));
+}
+
+int attn_kv_write(const void* k_new, const void* v_new, void* k_store, void* v_store,
+                  const int64_t* positions, const int32_t* seq_cols, const int32_t* slot_rows,
+                  int T, int Hkv, int D, int rows, int cols, const int64_t kn_str[3],
+                  const int64_t vn_str[3], const int64_t ks_str[4], const int64_t vs_str[4],
+                  void* workspace, size_t ws_bytes, void* stream) {
+    clear_err();
+    if (!k_store || !v_store) return fail(ATTN_ERR_INVALID, "null store pointer");
+    if (T > 0 && (!k_new || !v_new || !positions || !seq_cols))
+        return fail(ATTN_ERR_INVALID, "null tensor pointer");
+    if (!kn_str || !vn_str || !ks_str || !vs_str) return fail(ATTN_ERR_INVALID, "null stride array");
+    if (T < 0 || Hkv < 1 || D < 1 || rows < 1 || cols < 1)
+        return fail(ATTN_ERR_INVALID, "sizes must satisfy T >= 0 and Hkv, D, rows, cols >= 1");
+    if (D % 8 != 0 || D > 1024) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: a multiple of 8 up to 1024", D);
+    int st;
+    if ((st = check_layout("k_new", k_new, kn_str, 3))) return st;
+    if ((st = check_layout("v_new", v_new, vn_str, 3))) return st;
+    if ((st = check_layout("k_store", k_store, ks_str, 4))) return st;
+    if ((st = check_layout("v_store", v_store, vs_str, 4))) return st;
+    if ((uintptr_t)positions % 8 != 0 || (uintptr_t)seq_cols % 4 != 0 ||
+        (uintptr_t)slot_rows % 4 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "per-token arrays are not naturally aligned");
+    const int64_t nsz[3] = {T, Hkv, D}, ssz[4] = {rows, cols, Hkv, D};
+    if (!offset_ok(nsz, kn_str, 3) || !offset_ok(nsz, vn_str, 3) || !offset_ok(ssz, ks_str, 4) ||
+        !offset_ok(ssz, vs_str, 4))
+        return fail(ATTN_ERR_INVALID, "element offsets exceed 2^62");
+    const size_t need = attn_kv_write_workspace(T);
+    if (!workspace || ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (T == 0) return ATTN_OK;
+    KVWriteArgs a;
+    a.kn = (const u16*)k_new;
+    a.vn = (const u16*)v_new;
+    a.ks = (u16*)k_store;
+    a.vs = (u16*)v_store;
+    a.pos = positions;
+    a.col = seq_cols;
+    a.srows = slot_rows;
+    a.err = (int32_t*)workspace;
+    a.T = T;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.rows = rows;
+    a.cols = cols;
+    for (int i = 0; i < 3; ++i) {
+        a.kns[i] = kn_str[i];
+        a.vns[i] = vn_str[i];
+    }
+    for (int i = 0; i < 4; ++i) {
+        a.kss[i] = ks_str[i];
+        a.vss[i] = vs_str[i];
+    }
+    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)kv_write_blocks(T)),
+                       dim3(kWriteTokens * kWave), 0, (hipStream_t)stream, a);
+    if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "slot-write launch failed");
+    return ATTN_OK;
+}
+
+int attn_kv_write_read_error(const void* workspace, int T, void* stream, int32_t* err_out) {
+    clear_err();
+    if (!workspace || !err_out) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (T < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    *err_out = 0;
+    const int n = kv_write_blocks(T);
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "stream sync failed");
+    if (n == 0) return ATTN_OK;
+    std::vector<int32_t> host((size_t)n);
+    if (hipMemcpy(host.data(), workspace, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "copy of the error word failed");
+    int32_t e = 0;
+    for (int v : host) e |= v;
     *err_out = e;
     return ATTN_OK;
 }

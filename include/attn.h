@@ -43,6 +43,12 @@ typedef enum {
 #define ATTN_SEG_OVERLAP 16 /* a packed row claimed by two valid segments; the
                                outputs of those rows are then unspecified          */
 
+/* Bits of the slot-write error word (attn_kv_write_read_error).  A flagged
+ * token is not written. */
+#define ATTN_KV_COL 1  /* seq_cols[i] outside [0, cols)            */
+#define ATTN_KV_POS 2  /* positions[i] < 0                         */
+#define ATTN_KV_ROWS 4 /* slot_rows[i] > rows                      */
+
 /* Version of this ABI; bumped on any incompatible change. */
 int attn_abi_version(void);
 
@@ -149,6 +155,52 @@ int attn_sdpa_varlen(const void *q, const void *k_store, const void *v_store, vo
  */
 int attn_varlen_read_error(const void *workspace, int S, int T, void *stream,
                            int32_t *err_out);
+
+/*
+ * The step's K/V slot write, the operation before attn_sdpa_varlen.
+ *
+ * Defines ("[executorch][cuda] Add a length-aware Triton SDPA over
+ * per-sequence KV columns", the stacked commits on the batched-sequence
+ * manifest layout and the batched sequence cache): each step token i is
+ * written to slot (position mod rows) x columns + seq_cols[i] of the
+ * [rows, cols, Hkv, D] stores, i.e. store row positions[i] mod R_i of column
+ * seq_cols[i], where R_i is the token's ring rows (ring storage) or the store
+ * rows (flat storage); the last column is scratch for padded writes.
+ *
+ *   k_new, v_new     [T, Hkv, D] bf16 (read), strides kn_str[3], vn_str[3]
+ *   k_store, v_store [rows, cols, Hkv, D] bf16 (written), strides ks_str[4],
+ *                    vs_str[4]; must not overlap k_new / v_new
+ *   positions        [T] int64, device: absolute position of each token
+ *   seq_cols         [T] int32, device: column of each token's sequence
+ *   slot_rows        [T] int32, device, nullable: R_i (<= 0 or NULL: rows)
+ *
+ * Tokens whose column lies outside [0, cols), whose position is negative or
+ * whose R_i exceeds rows are skipped and flagged in the error word
+ * (ATTN_KV_*).  When two tokens of one call share a slot the slot receives
+ * one of them, unspecified which (only padded writes to the scratch column
+ * are expected to share).  The host never reads the per-token arrays, so
+ * one captured graph serves any positions and columns written into them.
+ *
+ * Layout rules (else ATTN_ERR_UNSUPPORTED): D a multiple of 8 up to 1024;
+ * innermost stride 1; other strides multiples of 8 elements; base pointers
+ * 16-byte aligned, positions 8-byte and seq_cols / slot_rows 4-byte
+ * aligned.  Sizes (else ATTN_ERR_INVALID): T >= 0, Hkv, D, rows, cols >= 1,
+ * element offsets below 2^62, non-null pointers (per-token arrays and new
+ * rows only when T > 0).  T == 0 enqueues nothing.
+ *
+ * workspace: at least attn_kv_write_workspace(T) bytes, 256-byte aligned;
+ * it holds the error word, read by attn_kv_write_read_error (which
+ * synchronises `stream`; T must be that of the call).
+ */
+size_t attn_kv_write_workspace(int T);
+
+int attn_kv_write(const void *k_new, const void *v_new, void *k_store, void *v_store,
+                  const int64_t *positions, const int32_t *seq_cols, const int32_t *slot_rows,
+                  int T, int Hkv, int D, int rows, int cols, const int64_t kn_str[3],
+                  const int64_t vn_str[3], const int64_t ks_str[4], const int64_t vs_str[4],
+                  void *workspace, size_t ws_bytes, void *stream);
+
+int attn_kv_write_read_error(const void *workspace, int T, void *stream, int32_t *err_out);
 
 /*
  * Profiling aid (not part of the computation).  After attn_timing_begin(),

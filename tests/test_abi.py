@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -215,3 +215,48 @@ def test_timing_clock_needs_recorded_sums():
     # no attention kernel ran, so there are no sums: an error, outputs cleared
     assert L.attn_timing_clock(ctypes.byref(mhz), per) == attn.ATTN_ERR_HIP
     assert mhz.value == 0.0 and list(per) == [0.0] * 8
+
+
+def _kvw(kn=A, vn=A, ks=A, vs=A, pos=A, col=A, srows=None, T=4, Hkv=2, D=64, rows=32, cols=3,
+         kns=None, vns=None, kss=None, vss=None, ws=A, ws_bytes=1024):
+    L = _lib()
+    kns = kns or _s(Hkv * D, D, 1)
+    vns = vns or _s(Hkv * D, D, 1)
+    kss = kss or _s(cols * Hkv * D, Hkv * D, D, 1)
+    vss = vss or _s(cols * Hkv * D, Hkv * D, D, 1)
+    return L.attn_kv_write(kn, vn, ks, vs, pos, col, srows, T, Hkv, D, rows, cols, kns, vns,
+                           kss, vss, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), attn.ATTN_ERR_INVALID),
+    (dict(pos=None), attn.ATTN_ERR_INVALID),
+    (dict(col=None), attn.ATTN_ERR_INVALID),
+    (dict(kn=None), attn.ATTN_ERR_INVALID),
+    (dict(T=-1), attn.ATTN_ERR_INVALID),
+    (dict(rows=0), attn.ATTN_ERR_INVALID),
+    (dict(D=60), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(kns=_s(128, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(kss=_s(384, 128, 60, 1)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=A + 8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(pos=A + 4), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws=A + 16), attn.ATTN_ERR_WORKSPACE),
+])
+def test_kv_write_validation(kw, code):
+    assert _kvw(**kw) == code, attn.lib().attn_last_error()
+
+
+def test_kv_write_zero_tokens_is_a_no_op_and_reads_no_error():
+    """T == 0 enqueues nothing (no GPU needed); its error word reads 0."""
+    L = _lib()
+    assert _kvw(T=0, kn=None, vn=None, pos=None, col=None) == attn.ATTN_OK
+    assert L.attn_kv_write_workspace(0) == 256
+    assert L.attn_kv_write_workspace(5) == 256
+    assert L.attn_kv_write_workspace(4 * 64 + 1) == 512
+
+
+def test_kv_write_flags_match_the_oracle_bits():
+    assert (attn.KV_COL, attn.KV_POS, attn.KV_ROWS) == (oracle.KVF_COL, oracle.KVF_POS,
+                                                         oracle.KVF_ROWS)
