@@ -236,11 +236,20 @@ def bench_prefill(args, name):
     dev = torch.device("cuda:0")
     q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
     out = torch.empty_like(q)
-    ws_bytes = attn.prefill_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
+    device_bound = args.bound == "device"
+    if device_bound:
+        # the same call with (q_pos0, kv_len) read from device memory
+        bounds = torch.tensor([q_pos0, Lkv], dtype=torch.int64, device=dev)
+        ws_bytes = attn.prefill_dev_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
+    else:
+        ws_bytes = attn.prefill_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        attn.causal_prefill(q, k, v, out=out, q_pos0=q_pos0, workspace=ws)
+        if device_bound:
+            attn.causal_prefill_dev(q, k, v, bounds, out=out, workspace=ws)
+        else:
+            attn.causal_prefill(q, k, v, out=out, q_pos0=q_pos0, workspace=ws)
 
     ms, kms, clk = time_calls(step, args.steps, args.warmup)
     proto = protocol_stats(step, args.steps)
@@ -253,8 +262,9 @@ def bench_prefill(args, name):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal GQA prefill %s" % name, "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "D": D, "Lq": Lq, "Lkv": Lkv, "q_pos0": q_pos0,
+        "config": {"workload": "causal GQA prefill %s%s" % (name, ", device bound" if device_bound
+                                                               else ""),
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Lq": Lq, "Lkv": Lkv, "q_pos0": q_pos0,
                    "unmasked_pairs": pairs},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": with_clock(
@@ -448,6 +458,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="d128_lq1k_lkv128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bound", choices=("host", "device"), default="host",
+                    help="prefill: q_pos0 and Lkv from the call, or read from device memory")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 256 MiB copy (counter calibration)")
     args = ap.parse_args()

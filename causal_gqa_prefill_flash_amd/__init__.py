@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP = 1, 2, 4, 8, 16
 KV_COL, KV_POS, KV_ROWS = 1, 2, 4
+BOUND_KV, BOUND_QPOS = 1, 2
 
 
 class AttnError(RuntimeError):
@@ -48,6 +49,13 @@ def lib():
     L.attn_causal_prefill.restype = I
     L.attn_causal_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float,
                                       I64A, I64A, I64A, I64A, I64, I, P, SZ, P]
+    L.attn_causal_prefill_dev_workspace.restype = SZ
+    L.attn_causal_prefill_dev_workspace.argtypes = [I, I, I, I, I, I]
+    L.attn_causal_prefill_dev.restype = I
+    L.attn_causal_prefill_dev.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float,
+                                          I64A, I64A, I64A, I64A, P, I, P, SZ, P]
+    L.attn_prefill_read_error.restype = I
+    L.attn_prefill_read_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
     L.attn_sdpa_varlen_workspace.restype = SZ
     L.attn_sdpa_varlen_workspace.argtypes = [I, I, I, I, I, I, I]
     L.attn_sdpa_varlen.restype = I
@@ -151,6 +159,48 @@ def causal_prefill(q, k, v, out=None, scale=None, q_pos0=None, window=0, workspa
             int(q_pos0), int(window), _ptr(ws), need, _stream())
     _check(st)
     return out
+
+
+def prefill_dev_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D):
+    return lib().attn_causal_prefill_dev_workspace(B, Hq, Hkv, Lq, Lkv, D)
+
+
+def causal_prefill_dev(q, k, v, bounds, out=None, scale=None, window=0, workspace=None):
+    """causal_prefill with a device-resident bound: ``bounds`` is a device
+    int64 tensor [2] = (q_pos0, kv_len); k/v [B,Hkv,Lkv,D] hold Lkv >= kv_len
+    keys of capacity.  Returns (out, workspace); read the bound flags with
+    ``prefill_read_error(workspace)``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _gpu(t, n)
+    if bounds.dtype != torch.int64 or not bounds.is_cuda or not bounds.is_contiguous() or \
+            bounds.numel() != 2:
+        raise ValueError("bounds must be a contiguous int64 device tensor of 2 entries")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not agree: %s %s %s" % (q.shape, k.shape, v.shape))
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _gpu(out, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        need = prefill_dev_workspace_bytes(B, Hq, Hkv, Lq, Lkv, D)
+        ws = _workspace(need, q.device, workspace)
+        st = lib().attn_causal_prefill_dev(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lkv, D, float(scale),
+            _strides(q, 4), _strides(k, 4), _strides(v, 4), _strides(out, 4), _ptr(bounds),
+            int(window), _ptr(ws), need, _stream())
+    _check(st)
+    return out, ws
+
+
+def prefill_read_error(workspace):
+    """The ATTN_BOUND_* flags of the last device-bound prefill on ``workspace``."""
+    e = ctypes.c_int32(0)
+    _check(lib().attn_prefill_read_error(_ptr(workspace), _stream(), ctypes.byref(e)))
+    return e.value
 
 
 def varlen_workspace_bytes(S, T, Hq, Hkv, D, rows, cols):

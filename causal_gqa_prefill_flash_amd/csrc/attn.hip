@@ -883,6 +883,10 @@ __device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
 
 // ---------------------------------------------------------------- prefill
 
+// Largest magnitude of a query position read from the device (larger ones
+// are clamped and flagged).
+constexpr int64_t kBoundPos = (int64_t)1 << 62;
+
 // Shader-clock sampling for the timing aid.  Thread 0 of each workgroup reads
 // the shader cycle counter (s_memtime) and the constant 100 MHz reference
 // counter (s_memrealtime) when it starts and when it is done, and adds both
@@ -932,6 +936,8 @@ struct PrefillArgs {
     int64_t q_pos0;
     int64_t qs[4], ks[4], vs[4], os[4];
     unsigned long long* clk;  // timing aid: per-XCD clock sums, or null
+    const int64_t* bounds;    // device (q_pos0, kv_len) replacing q_pos0 and Lkv, or null
+    int32_t* err;             // with bounds: the bound flags, written by workgroup 0
 };
 
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id.  Map
@@ -972,8 +978,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int heads_here = min(rm.Gc, g - hc * rm.Gc);
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int64_t p_min = a.q_pos0 + q0;
-    const int64_t p_max = a.q_pos0 + min(q0 + rm.P, a.Lq) - 1;
+    // the key bound and the first row's position: from the call, or read on
+    // the device (Lkv is then the capacity: a larger bound is clamped to it)
+    int64_t q_pos0 = a.q_pos0;
+    int Lkv = a.Lkv;
+    if (a.bounds) {
+        const int64_t qp = a.bounds[0], kl = a.bounds[1];
+        q_pos0 = qp < -kBoundPos ? -kBoundPos : (qp > kBoundPos ? kBoundPos : qp);
+        Lkv = kl < 0 ? 0 : (kl > a.Lkv ? a.Lkv : (int)kl);
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            a.err[0] = (kl < 0 || kl > a.Lkv ? ATTN_BOUND_KV : 0) |
+                       (qp != q_pos0 ? ATTN_BOUND_QPOS : 0);
+    }
+    const int64_t p_min = q_pos0 + q0;
+    const int64_t p_max = q_pos0 + min(q0 + rm.P, a.Lq) - 1;
 
     // this lane's row in each of the wave's row tiles
     int hrow[kNT], irow[kNT];
@@ -987,7 +1005,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         irow[nt] = q0 + pos;
         hrow[nt] = hk * g + hc * rm.Gc + hl;
         valid[nt] = hl < heads_here && irow[nt] < a.Lq;
-        p_lane[nt] = valid[nt] ? a.q_pos0 + irow[nt] : p_max;
+        p_lane[nt] = valid[nt] ? q_pos0 + irow[nt] : p_max;
         load_q<D>(qf[nt],
                   a.q + b * a.qs[0] + (int64_t)hrow[nt] * a.qs[1] + (int64_t)irow[nt] * a.qs[2],
                   valid[nt], a.negate);
@@ -995,7 +1013,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
     // visible keys of the whole workgroup, then this split's share
     int64_t lo64 = a.window > 0 ? p_min - a.window + 1 : 0;
-    int64_t hi64 = p_max + 1 < a.Lkv ? p_max + 1 : a.Lkv;
+    int64_t hi64 = p_max + 1 < Lkv ? p_max + 1 : Lkv;
     if (lo64 < 0) lo64 = 0;
     if (hi64 < lo64) hi64 = lo64;
     int k_lo, k_hi;
@@ -1806,11 +1824,13 @@ size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, in
     return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus));
 }
 
-int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, int B, int Hq,
-                        int Hkv, int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
-                        const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
-                        int64_t q_pos0, int window, void* workspace, size_t ws_bytes,
-                        void* stream) {
+// Both prefill entry points: with bounds (device (q_pos0, kv_len)), the
+// workspace starts with the 256-byte error word and the partials follow.
+int prefill_call(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                 int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
+                 const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
+                 int64_t q_pos0, const int64_t* bounds, int window, void* workspace,
+                 size_t ws_bytes, void* stream) {
     clear_err();
     if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0)
@@ -1835,12 +1855,15 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     if (!offset_ok(qsz, q_str, 4) || !offset_ok(ksz, k_str, 4) || !offset_ok(ksz, v_str, 4) ||
         !offset_ok(qsz, o_str, 4))
         return fail(ATTN_ERR_INVALID, "element offsets exceed 2^62");
+    if (bounds && (uintptr_t)bounds % 8 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "bounds is not 8-byte aligned");
     if (Lq == 0) return ATTN_OK;
 
     DeviceInfo di;
     if ((st = device_info(&di))) return st;
     const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus);
-    const size_t need = prefill_ws_bytes(B, Hq, Lq, D, nsplit);
+    const size_t errb = bounds ? 256 : 0;
+    const size_t need = errb + prefill_ws_bytes(B, Hq, Lq, D, nsplit);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? ws_bytes : (size_t)0);
@@ -1853,8 +1876,12 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
     a.v = (const u16*)v;
     a.out = (u16*)out;
     size_t prow = (size_t)nsplit * B * Hq * Lq;
-    a.part_o = need ? (float*)workspace : nullptr;
-    a.part_ml = need ? (float*)((char*)workspace + align256(prow * D * sizeof(float))) : nullptr;
+    const bool parts = need > errb;
+    a.part_o = parts ? (float*)((char*)workspace + errb) : nullptr;
+    a.part_ml =
+        parts ? (float*)((char*)workspace + errb + align256(prow * D * sizeof(float))) : nullptr;
+    a.bounds = bounds;
+    a.err = bounds ? (int32_t*)workspace : nullptr;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -1899,6 +1926,49 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
             hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)nb), dim3(256), 0, s, a);
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch failed");
     }
+    return ATTN_OK;
+}
+
+int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, int B, int Hq,
+                        int Hkv, int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
+                        const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
+                        int64_t q_pos0, int window, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    return prefill_call(q, k, v, out, B, Hq, Hkv, Lq, Lkv, D, scale, q_str, k_str, v_str, o_str,
+                        q_pos0, nullptr, window, workspace, ws_bytes, stream);
+}
+
+size_t attn_causal_prefill_dev_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0 || Hq % Hkv != 0) return 0;
+    if (D != 64 && D != 128) return 0;
+    return 256 + attn_causal_prefill_workspace(B, Hq, Hkv, Lq, Lkv, D);
+}
+
+int attn_causal_prefill_dev(const void* q, const void* k, const void* v, void* out, int B,
+                            int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                            const int64_t q_str[4], const int64_t k_str[4],
+                            const int64_t v_str[4], const int64_t o_str[4],
+                            const int64_t* bounds, int window, void* workspace, size_t ws_bytes,
+                            void* stream) {
+    if (!bounds) {
+        clear_err();
+        return fail(ATTN_ERR_INVALID, "null bounds");
+    }
+    if (Lq > 0 && (!workspace || ws_bytes < 256)) {
+        clear_err();
+        return fail(ATTN_ERR_WORKSPACE, "workspace of at least 256 bytes needed");
+    }
+    return prefill_call(q, k, v, out, B, Hq, Hkv, Lq, Lkv, D, scale, q_str, k_str, v_str, o_str,
+                        0, bounds, window, workspace, ws_bytes, stream);
+}
+
+int attn_prefill_read_error(const void* workspace, void* stream, int32_t* err_out) {
+    clear_err();
+    if (!workspace || !err_out) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "stream sync failed");
+    if (hipMemcpy(err_out, workspace, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "copy of the error word failed");
     return ATTN_OK;
 }
 

@@ -49,6 +49,10 @@ typedef enum {
 #define ATTN_KV_POS 2  /* positions[i] < 0                         */
 #define ATTN_KV_ROWS 4 /* slot_rows[i] > rows                      */
 
+/* Bits of the device-bound prefill's error word (attn_prefill_read_error). */
+#define ATTN_BOUND_KV 1   /* kv_len outside [0, Lkv]: clamped into it          */
+#define ATTN_BOUND_QPOS 2 /* |q_pos0| above 2^62: clamped                       */
+
 /* Version of this ABI; bumped on any incompatible change. */
 int attn_abi_version(void);
 
@@ -96,6 +100,37 @@ int attn_causal_prefill(const void *q, const void *k, const void *v, void *out,
                         const int64_t v_str[4], const int64_t o_str[4],
                         int64_t q_pos0, int window,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The same prefill with a device-resident KV bound.
+ *
+ * Defines ("[CUDA] Use Triton TMA for long-context causal prefill",
+ * Summary: the long-context path is chosen for global causal attention with
+ * a KV bound that lives on the device): bounds is a device int64[2] =
+ * (q_pos0, kv_len), read by the kernels, so one captured graph serves every
+ * chunk of a chunked prefill whose start position and key count change
+ * between replays.  Lkv is then the capacity of the K/V tensors: keys
+ * [0, kv_len) exist, a kv_len outside [0, Lkv] is clamped into it and
+ * flagged (ATTN_BOUND_KV), a |q_pos0| above 2^62 is clamped and flagged
+ * (ATTN_BOUND_QPOS).  Everything else is as attn_causal_prefill with
+ * q_pos0 = bounds[0] and Lkv = kv_len; the key splits follow the capacity.
+ *
+ * workspace: attn_causal_prefill_dev_workspace(...) bytes (at least 256),
+ * 256-byte aligned: the error word, then the split partials.
+ * attn_prefill_read_error synchronises `stream` and reads the error word of
+ * the last call that used this workspace.  bounds must be 8-byte aligned
+ * (else ATTN_ERR_UNSUPPORTED) and non-null (else ATTN_ERR_INVALID).
+ */
+size_t attn_causal_prefill_dev_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D);
+
+int attn_causal_prefill_dev(const void *q, const void *k, const void *v, void *out,
+                            int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                            const int64_t q_str[4], const int64_t k_str[4],
+                            const int64_t v_str[4], const int64_t o_str[4],
+                            const int64_t *bounds, int window,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+int attn_prefill_read_error(const void *workspace, void *stream, int32_t *err_out);
 
 /*
  * Length-aware varlen SDPA over per-sequence KV columns.

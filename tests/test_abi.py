@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -260,3 +260,19 @@ def test_kv_write_zero_tokens_is_a_no_op_and_reads_no_error():
 def test_kv_write_flags_match_the_oracle_bits():
     assert (attn.KV_COL, attn.KV_POS, attn.KV_ROWS) == (oracle.KVF_COL, oracle.KVF_POS,
                                                          oracle.KVF_ROWS)
+
+
+def test_prefill_dev_needs_bounds_and_an_error_word():
+    L = _lib()
+    D, Hq, Hkv, Lq, Lkv = 64, 4, 2, 8, 16
+    qs = _s(Hq * Lq * D, Lq * D, D, 1)
+    ks = _s(Hkv * Lkv * D, Lkv * D, D, 1)
+    args = (A, A, A, A, 1, Hq, Hkv, Lq, Lkv, D, 0.125, qs, ks, ks, qs)
+    assert L.attn_causal_prefill_dev(*args, None, 0, A, 4096, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_causal_prefill_dev(*args, A, 0, None, 0, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_causal_prefill_dev(*args, A, 0, A, 128, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_causal_prefill_dev(*args, A + 4, 0, A, 4096, None) == attn.ATTN_ERR_UNSUPPORTED
+    # Lq == 0 enqueues nothing
+    args0 = (A, A, A, A, 1, Hq, Hkv, 0, Lkv, D, 0.125, qs, ks, ks, qs)
+    assert L.attn_causal_prefill_dev(*args0, A, 0, None, 0, None) == attn.ATTN_OK
+    assert (attn.BOUND_KV, attn.BOUND_QPOS) == (1, 2)
