@@ -62,10 +62,10 @@ struct RowMap {
     int Gc, P, hchunks;
 };
 
-__host__ __device__ inline RowMap row_map(int g) {
+__host__ __device__ inline RowMap row_map(int g, int bm = kBM) {
     RowMap r;
-    r.Gc = g < kBM ? g : kBM;
-    r.P = kBM / r.Gc;
+    r.Gc = g < bm ? g : bm;
+    r.P = bm / r.Gc;
     r.hchunks = (g + r.Gc - 1) / r.Gc;
     return r;
 }
@@ -126,7 +126,9 @@ struct KVRing {
 // position c ^ swz(r).
 template <int D>
 __device__ __host__ constexpr int swz(int r) {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    // D = 256 rows (512 bytes) start on the same bank as D = 128 rows, so
+    // they take the same pattern on the low four chunk bits
+    return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -1041,6 +1043,159 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     clock_add(a.clk, cm);
 }
 
+// ---------------------------------------------------------------- D = 256
+//
+// Head dimension 256 does not fit the ping-pong kernel: a wave's 32 rows
+// hold 128 accumulator and 64 query-fragment registers, so only one wave
+// fits per SIMD.  The workgroup is four waves (128 rows, one wave per SIMD)
+// over 64-key K and V tiles double-buffered in LDS (4 x 32 KB): while the
+// waves compute tile t, the copies of tile t+1 are in flight.  Each tile
+// takes the exact online softmax (running maximum and rescale).
+
+constexpr int kWaves256 = 4;
+constexpr int kBM256 = kWaves256 * 32;
+
+// This wave's share (instructions w, w + 4, ...) of the copy of keys
+// [k0, k0 + 64) of one tensor of flat storage into an LDS tile; rows at or
+// past k_hi repeat row k_hi - 1 (their scores are masked).
+__device__ inline void copy_tile256(const u16* base, int64_t rs, int k0, int k_hi, u16* dst) {
+    constexpr int D = 256, CH = D / 8, ROWS = 64 / CH, INSTR = kBN / ROWS;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < INSTR / kWaves256; ++j) {
+        const int i = w + j * kWaves256;
+        const int r = i * ROWS + lane / CH;
+        const int k = min(k0 + r, k_hi - 1);
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(base + (int64_t)k * rs + 8 * ((lane % CH) ^ swz<D>(r))),
+            (lds_void*)(dst + i * 512), 16, 0, 0);
+    }
+}
+
+// One key tile of the D = 256 loop: copies of the next tile into (Kn, Vn)
+// go out first, then the wave waits for its copies of this tile and the
+// workgroup barrier makes every wave's copies visible; scores, mask, exact
+// softmax, PV; a closing barrier frees (Kc, Vc) for the copies two tiles on.
+__device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_t vrs, int t,
+                               int n, int k_lo, int k_hi, int t_in0, int t_in1,
+                               const bf16x8 (*qf)[16], const LaneBounds* lb, float c,
+                               RowState<256>& st, const u16* Kc, const u16* Vc, u16* Kn, u16* Vn) {
+    constexpr int D = 256;
+    if (t + 1 < n) {
+        copy_tile256(kb, krs, k_lo + (t + 1) * kBN, k_hi, Kn);
+        copy_tile256(vb, vrs, k_lo + (t + 1) * kBN, k_hi, Vn);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kBN / (64 / (D / 8))) / kWaves256));
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __builtin_amdgcn_s_barrier();
+    TileScores S;
+    qk_tile<D>(Kc, qf, S, NoCopy{}, NoCopy{});
+    if (t < t_in0 || t >= t_in1) mask_tile(S, k_lo + t * kBN, lb);
+    float alpha[kNT], lsum[kNT];
+    update_max(S, c, st.m, alpha);
+    rescale<D>(alpha, st);
+    TileP pk;
+    softmax_tile(S, c, st.m, pk, lsum);
+    st.l[0] += lsum[0];
+    pv_tile<D>(Vc, pk, st, NoCopy{});
+    __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(PrefillArgs a) {
+    constexpr int D = 256;
+    __shared__ __attribute__((aligned(1024))) u16 sk0[kBN * D];
+    __shared__ __attribute__((aligned(1024))) u16 sv0[kBN * D];
+    __shared__ __attribute__((aligned(1024))) u16 sk1[kBN * D];
+    __shared__ __attribute__((aligned(1024))) u16 sv1[kBN * D];
+    const ClockMark cm = clock_mark(a.clk);
+
+    const int g = a.Hq / a.Hkv;
+    const RowMap rm = row_map(g, kBM256);
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int inner = w % a.n_inner, outer = w / a.n_inner;
+    const int qb = inner / rm.hchunks, hc = inner % rm.hchunks;
+    const int split = outer % a.nsplit, bh = outer / a.nsplit;
+    const int b = bh / a.Hkv, hk = bh % a.Hkv;
+    const int q0 = qb * rm.P;
+    const int heads_here = min(rm.Gc, g - hc * rm.Gc);
+
+    int64_t q_pos0 = a.q_pos0;
+    int Lkv = a.Lkv;
+    if (a.bounds) {
+        const int64_t qp = a.bounds[0], kl = a.bounds[1];
+        q_pos0 = qp < -kBoundPos ? -kBoundPos : (qp > kBoundPos ? kBoundPos : qp);
+        Lkv = kl < 0 ? 0 : (kl > a.Lkv ? a.Lkv : (int)kl);
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            a.err[0] = (kl < 0 || kl > a.Lkv ? ATTN_BOUND_KV : 0) |
+                       (qp != q_pos0 ? ATTN_BOUND_QPOS : 0);
+    }
+    const int64_t p_min = q_pos0 + q0;
+    const int64_t p_max = q_pos0 + min(q0 + rm.P, a.Lq) - 1;
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int r = wave * 32 + (lane & 31);
+    const int hl = r / rm.P, pos = r % rm.P;
+    const int irow = q0 + pos, hrow = hk * g + hc * rm.Gc + hl;
+    const bool valid = hl < heads_here && irow < a.Lq;
+    const int64_t p_lane = valid ? q_pos0 + irow : p_max;
+    bf16x8 qf[1][D / 16];
+    load_q<D>(qf[0], a.q + b * a.qs[0] + (int64_t)hrow * a.qs[1] + (int64_t)irow * a.qs[2], valid,
+              a.negate);
+
+    int64_t lo64 = a.window > 0 ? p_min - a.window + 1 : 0;
+    int64_t hi64 = p_max + 1 < Lkv ? p_max + 1 : Lkv;
+    if (lo64 < 0) lo64 = 0;
+    if (hi64 < lo64) hi64 = lo64;
+    int k_lo, k_hi;
+    split_range((int)lo64, (int)hi64, split, a.nsplit, &k_lo, &k_hi);
+
+    RowState<D> st;
+    init_state<D>(st);
+    if (k_lo < k_hi) {
+        const int n = (k_hi - k_lo + kBN - 1) / kBN;
+        // tiles t_in0 <= t < t_in1 need no mask (as interior_tiles)
+        int64_t t1 = (k_hi - k_lo) / kBN;
+        {
+            const int64_t cc = p_min - k_lo - (kBN - 1);
+            const int64_t tc = cc < 0 ? 0 : cc / kBN + 1;
+            if (tc < t1) t1 = tc;
+        }
+        int64_t t0 = 0;
+        if (a.window > 0) {
+            const int64_t ww = p_max - a.window - k_lo;
+            t0 = ww < 0 ? 0 : ww / kBN + 1;
+        }
+        if (t1 > n) t1 = n;
+        if (t0 > t1) t0 = t1;
+        const LaneBounds lb = lane_bounds(k_lo, k_hi, 1, a.window, p_lane);
+        const u16* kb = a.k + b * a.ks[0] + hk * a.ks[1];
+        const u16* vb = a.v + b * a.vs[0] + hk * a.vs[1];
+        copy_tile256(kb, a.ks[2], k_lo, k_hi, sk0);
+        copy_tile256(vb, a.vs[2], k_lo, k_hi, sv0);
+        for (int t = 0; t < n; t += 2) {
+            tile256(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb, a.c, st,
+                    sk0, sv0, sk1, sv1);
+            if (t + 1 < n)
+                tile256(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
+                        a.c, st, sk1, sv1, sk0, sv0);
+        }
+    }
+
+    if (a.nsplit == 1) {
+        store_out<D>(st.o[0], st.l[0],
+                     a.out + b * a.os[0] + (int64_t)hrow * a.os[1] + (int64_t)irow * a.os[2],
+                     valid);
+    } else {
+        const int64_t row =
+            (((int64_t)split * a.B + b) * a.Hq + hrow) * a.Lq + irow;
+        store_partial<D>(st.o[0], st.m[0], st.l[0], a.c, a.part_o + row * D, a.part_ml + row * 2,
+                         valid);
+    }
+    clock_add(a.clk, cm);
+}
+
 // Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
 // o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).  The splits are
 // read in groups of 8 whose loads are all in flight together (indices past
@@ -1751,7 +1906,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // split.
 int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
-    RowMap rm = row_map(Hq / Hkv);
+    RowMap rm = row_map(Hq / Hkv, D == 256 ? kBM256 : kBM);
     int64_t base = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks * B * Hkv;
     int by_keys = (Lkv + 1023) / 1024;
     if (by_keys < 1) by_keys = 1;
@@ -1817,7 +1972,7 @@ const char* attn_last_error(void) { return g_err; }
 
 size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0 || Hq % Hkv != 0) return 0;
-    if (D != 64 && D != 128) return 0;
+    if (D != 64 && D != 128 && D != 256) return 0;
     if (Lq == 0) return 0;
     DeviceInfo di;
     if (device_info(&di) != ATTN_OK) return 0;
@@ -1840,7 +1995,8 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
         return fail(ATTN_ERR_INVALID, "null tensor pointer");
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
     if (!(scale == scale) || isinf(scale)) return fail(ATTN_ERR_INVALID, "scale is not finite");
-    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only 64 and 128", D);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only 64, 128 and 256", D);
     if (q_pos0 > kMaxOffset || q_pos0 < -kMaxOffset)
         return fail(ATTN_ERR_INVALID, "q_pos0 out of range");
     int st;
@@ -1900,7 +2056,7 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
         a.vs[i] = v_str[i];
         a.os[i] = o_str[i];
     }
-    RowMap rm = row_map(Hq / Hkv);
+    RowMap rm = row_map(Hq / Hkv, D == 256 ? kBM256 : kBM);
     const int64_t n_inner = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks;
     const int64_t nwg = n_inner * B * Hkv * nsplit;
     if (nwg > 0x7fffffff)
@@ -1912,8 +2068,10 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
     hipEvent_t t0 = timing_start(s);
     if (D == 64)
         hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
-    else
+    else if (D == 128)
         hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(prefill256_kernel, grid, dim3(kWaves256 * kWave), 0, s, a);
     timing_stop(t0, s);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed");
     if (nsplit > 1) {
@@ -1922,8 +2080,10 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
         int64_t nb = (rows + per - 1) / per;
         if (D == 64)
             hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)nb), dim3(256), 0, s, a);
-        else
+        else if (D == 128)
             hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3((unsigned)nb), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(prefill_combine_kernel<256>, dim3((unsigned)nb), dim3(256), 0, s, a);
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch failed");
     }
     return ATTN_OK;
@@ -1940,7 +2100,7 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
 
 size_t attn_causal_prefill_dev_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0 || Hq % Hkv != 0) return 0;
-    if (D != 64 && D != 128) return 0;
+    if (D != 64 && D != 128 && D != 256) return 0;
     return 256 + attn_causal_prefill_workspace(B, Hq, Hkv, Lq, Lkv, D);
 }
 

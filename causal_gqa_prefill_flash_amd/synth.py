@@ -39,6 +39,9 @@ PREFILL_WORKLOADS = {
                                        q_pos0=-16),
     "d64_lq4k_lkv128k": dict(wid=4, B=1, Hq=16, Hkv=2, D=64, Lq=4096, Lkv=131072, q_pos0=None),
     "d128_lq4k_lkv128k": dict(wid=4, B=1, Hq=16, Hkv=2, D=128, Lq=4096, Lkv=131072, q_pos0=None),
+    # head dimension 256 on the long-context shape
+    "d256_lq1k_lkv128k": dict(wid=5, B=1, Hq=16, Hkv=2, D=256, Lq=1024, Lkv=131072, q_pos0=None),
+    "d256_lq512_lkv16k": dict(wid=6, B=1, Hq=16, Hkv=2, D=256, Lq=512, Lkv=16384, q_pos0=None),
 }
 
 # Varlen column store of the segment-table workload: [rows, cols, Hkv, D];

@@ -80,7 +80,9 @@ const char *attn_last_error(void);
  * o = sum_j softmax_j(scale * q.k_j) v_j over the visible keys; a row with
  * no visible key is written as exact zeros.
  *
- * Layout rules (else ATTN_ERR_UNSUPPORTED): D in {64, 128}; innermost
+ * Layout rules (else ATTN_ERR_UNSUPPORTED): D in {64, 128, 256} (256: the
+ * head dimension the page left on its portable path, here a kernel of its
+ * own); innermost
  * stride 1 on all four tensors; base pointers 16-byte aligned; every other
  * stride a multiple of 8 elements; k/v row strides (k_str[2], v_str[2])
  * below 2^24 elements.

@@ -70,7 +70,7 @@ def _prefill(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64, scale=0
     (dict(scale=float("nan")), attn.ATTN_ERR_INVALID),
     (dict(scale=float("inf")), attn.ATTN_ERR_INVALID),
     (dict(D=96), attn.ATTN_ERR_UNSUPPORTED),
-    (dict(D=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(D=512), attn.ATTN_ERR_UNSUPPORTED),
     (dict(qs=_s(4 * 8 * 64, 8 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),   # inner stride
     (dict(ks=_s(2 * 16 * 64, 16 * 64, 68, 1)), attn.ATTN_ERR_UNSUPPORTED),  # row not 16 B
     (dict(vs=_s(2 * 16 * 64, -16 * 64, 64, 1)), attn.ATTN_ERR_UNSUPPORTED),  # negative
@@ -133,6 +133,7 @@ def _varlen(S=2, T=16, Hq=4, Hkv=2, D=64, rows=32, cols=3, causal=1, window=0, r
     (dict(ring_rows=33), attn.ATTN_ERR_INVALID),         # ring larger than the store
     (dict(causal=0, window=4), attn.ATTN_ERR_INVALID),   # window without causality
     (dict(D=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(D=256), attn.ATTN_ERR_UNSUPPORTED),            # varlen: 64 and 128 only
     (dict(qs=_s(4 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),
     (dict(ks=_s(3 * 2 * 64, 2 * 64, 60, 1)), attn.ATTN_ERR_UNSUPPORTED),
     (dict(ws=None), attn.ATTN_ERR_WORKSPACE),

@@ -26,6 +26,9 @@ def _run(q, k, v, **kw):
     (1, 16, 2, 77, 3001, 128, None, 0),
     (1, 6, 2, 130, 700, 64, None, 0),     # g = 3: rows of a block are 3 heads x 42 positions
     (1, 4, 4, 200, 333, 128, 0, 0),       # MHA (g = 1)
+    (1, 16, 2, 300, 1000, 256, None, 0),  # D = 256: ragged, several q-blocks
+    (2, 8, 2, 129, 700, 256, 0, 0),       # D = 256: queries from position 0
+    (1, 8, 2, 200, 900, 256, None, 150),  # D = 256 with a window
     (1, 32, 1, 40, 500, 64, None, 0),     # g = 32
     (1, 8, 2, 257, 900, 128, None, 100),  # sliding window
     (1, 8, 2, 129, 129, 64, 0, 1),        # window of one key: returns V rows
@@ -33,6 +36,8 @@ def _run(q, k, v, **kw):
     (1, 8, 2, 64, 200, 64, -20, 0),       # 20 rows see nothing
     (1, 8, 2, 1, 5000, 128, None, 0),     # a single query row
     (1, 8, 2, 33, 0, 64, None, 0),        # no keys
+    (1, 8, 2, 64, 200, 256, -20, 0),      # D = 256: 20 rows see nothing
+    (1, 8, 2, 33, 0, 256, None, 0),       # D = 256: no keys
 ])
 def test_prefill_matches_oracle(B, Hq, Hkv, Lq, Lkv, D, q_pos0, window):
     say("prefill", B, Hq, Hkv, Lq, Lkv, D, q_pos0, window)
@@ -47,7 +52,7 @@ def test_prefill_matches_oracle(B, Hq, Hkv, Lq, Lkv, D, q_pos0, window):
         assert torch.count_nonzero(out[:, :, :-q_pos0]) == 0
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
 def test_forced_splits_match_oracle(D, splits, monkeypatch):
     monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
@@ -166,7 +171,7 @@ def _shifted_keys(k, q, scale, logit_of_key):
     return qpos, (k.float() + shift).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_logits_far_from_the_first_tile(D, direction):
     """Logits that rise along the keys by ~150 nats overflow the reference

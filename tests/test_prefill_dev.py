@@ -15,7 +15,7 @@ def _bounds(q_pos0, kv_len):
     return torch.tensor([q_pos0, kv_len], dtype=torch.int64, device=dev())
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_device_bound_equal_to_the_host_bound_gives_the_same_bits(D):
     say("prefill dev bound == host bound, D", D)
     B, Hq, Hkv, Lq, Lkv = 1, 16, 2, 300, 5000
@@ -28,7 +28,7 @@ def test_device_bound_equal_to_the_host_bound_gives_the_same_bits(D):
     compare(out, oracle.prefill(q, k, v, 1.0 / D ** 0.5, q_pos0=Lkv - Lq), "dev bound D%d" % D)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_chunked_prefill_replays_one_graph(D):
     """A 4096-key cache filled chunk by chunk: one captured graph, replayed
     for each 512-row chunk with the chunk's queries and (start, start + 512)
