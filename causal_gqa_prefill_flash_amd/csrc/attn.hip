@@ -1198,12 +1198,11 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
 
 // Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
 // o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).  The splits are
-// read in groups of 8 whose loads are all in flight together (indices past
+// read in groups of G whose loads are all in flight together (indices past
 // nsplit are clamped and weighted 0); groups merge by the same rule.
-template <int D>
+template <int D, int G = 8>
 __device__ inline void combine_row(const float* po, const float* pml, int64_t split_stride_o,
                                    int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
-    constexpr int G = 8;
     float M = -INFINITY, L = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsplit; s0 += G) {
@@ -1373,15 +1372,16 @@ __device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int gq, int 
 // sums the item counts of the segments ordered before them; one thread finds
 // the segment that holds L.  Returns false when L is past the last item.
 __device__ bool pick_item(const VarlenArgs& a, int P, int hg, int gq, int L, int* seg_out,
-                          int* j_out) {
+                          int* j_out, Segment* sg_out) {
     constexpr int NT = kThreads;  // one segment per thread per pass
     __shared__ int sh_cost[NT], sh_count[NT];
     __shared__ int sh_seg, sh_j;
+    __shared__ Segment sh_sg;
     if (threadIdx.x == 0) sh_seg = -1;
     for (int c0 = 0; c0 < a.S; c0 += NT) {
         const int s = c0 + threadIdx.x;
-        const SegPlan ps = s < a.S ? seg_plan(read_segment(a, s), P, hg, gq, a.Hkv, a.split_keys,
-                                              a.nsplit)
+        const Segment xs = s < a.S ? read_segment(a, s) : Segment{};
+        const SegPlan ps = s < a.S ? seg_plan(xs, P, hg, gq, a.Hkv, a.split_keys, a.nsplit)
                                    : SegPlan{0, 1, 0, 0, false};
         int64_t off = 0;
         for (int d0 = 0; d0 < a.S; d0 += NT) {
@@ -1404,11 +1404,13 @@ __device__ bool pick_item(const VarlenArgs& a, int P, int hg, int gq, int L, int
         if (s < a.S && ps.count > 0 && L >= off && L < off + ps.count) {
             sh_seg = s;
             sh_j = (int)(L - off);
+            sh_sg = xs;  // the picked segment, so no thread reads it again
         }
     }
     __syncthreads();
     *seg_out = sh_seg;
     *j_out = sh_j;
+    if (sh_seg >= 0) *sg_out = sh_sg;
     return sh_seg >= 0;
 }
 
@@ -1593,8 +1595,8 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 
     // this workgroup's work item: (segment, item j of that segment)
     int seg, j;
-    if (!pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j)) return;
-    const Segment sg = read_segment(a, seg);
+    Segment sg;
+    if (!pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j, &sg)) return;
     const SegPlan pl = seg_plan(sg, rm.P, hg, g, a.Hkv, a.split_keys, a.nsplit);
     if (pl.decode) {
         __shared__ __attribute__((aligned(1024))) u16 sx[2 * kBN * D];
@@ -1671,7 +1673,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 // (workgroup 0 also reports every segment's flags).
 template <int D>
 __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
-    __shared__ int flags_sh, owner_sh, count_sh;
+    __shared__ int flags_sh, owner_sh, count_sh, ns_sh;
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
     const int t = blockIdx.x;
@@ -1681,24 +1683,28 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
         count_sh = 0;
     }
     __syncthreads();
-    int flags = 0;
+    int flags = 0, mine = -1, my_ns = 1;
     for (int s = threadIdx.x; s < a.S; s += 256) {
         const Segment x = read_segment(a, s);
         if (blockIdx.x == 0) flags |= x.flags;
         if (!x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len) {
             atomicMin(&owner_sh, s);
             atomicAdd(&count_sh, 1);
+            if (mine < 0) {  // this thread's first (lowest) covering segment
+                mine = s;
+                my_ns = seg_plan(x, rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys, a.nsplit)
+                            .nsplit;
+            }
         }
     }
     if (flags) atomicOr(&flags_sh, flags);
     __syncthreads();
+    // the thread that read the owning segment publishes its split count
+    if (mine >= 0 && mine == owner_sh) ns_sh = my_ns;
+    __syncthreads();
     if (t < a.T) {
         const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
-        int ns = 1;
-        if (owner >= 0)
-            ns = seg_plan(read_segment(a, owner), rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys,
-                          a.nsplit)
-                     .nsplit;
+        const int ns = owner >= 0 ? ns_sh : 1;
         if (owner < 0 || ns > 1) {
             constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
             for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
@@ -1708,7 +1714,14 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
                     *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
                 } else {
                     const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
-                    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, D, 2, ns, d0, orow);
+                    // all of a row's loads in flight at once, in the narrower
+                    // group when it holds every split
+                    if (ns > 8)
+                        combine_row<D, kMaxVarlenSplits>(a.part_o + row * D, a.part_ml + row * 2,
+                                                         D, 2, ns, d0, orow);
+                    else
+                        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 2, D, 2, ns, d0,
+                                          orow);
                 }
             }
         }

@@ -111,6 +111,48 @@ def test_long_segment_rising_logits_split(D):
     assert torch.count_nonzero(out[:4]) == 0 and torch.count_nonzero(out[4 + q_len:]) == 0
 
 
+@pytest.mark.parametrize("D,Hq", [(128, 16), (64, 16), (128, 8)])
+def test_decode_items_of_every_row_count(D, Hq):
+    """Segments of 1..128 rows (q_len x g) run as decode items with 1, 2 or 4
+    row blocks per key stream; flat, ring and windowed, next to one another."""
+    say("varlen decode rows D", D, "Hq", Hq)
+    rows, cols, Hkv = 8192, 9, 2
+    g = Hq // Hkv
+    qlens = [1, 3, 4, 5, 8, 12, 16, 128 // g]
+    info, attr, t = [], [], 0
+    for s, ql in enumerate(qlens):
+        kv_end = 8192 - 301 * s if s % 3 else 6000 + 77 * s
+        ring = 2559 if s % 4 == 3 else 0
+        window = 2048 if ring else (700 if s == 5 else 0)
+        info.append((t, ql, s, kv_end))
+        attr.append((1, window, ring))
+        t += ql + 2
+    T = t + 3
+    info = torch.tensor(info, dtype=torch.int32)
+    attr = torch.tensor(attr, dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=48)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
+    assert err == 0
+    compare(out, ref, "decode rows D%d Hq%d" % (D, Hq))
+
+
+def test_two_segments_of_one_sequence():
+    """A sequence's owner rows (causal) and its draft block (non-causal) as
+    two segments over the same column, next to other sequences (up to
+    2 x (cols - 1) segments)."""
+    say("varlen two segments per sequence")
+    rows, cols, Hkv, D, Hq = 4096, 3, 2, 128, 16
+    info = torch.tensor([(0, 4, 1, 1000), (6, 16, 1, 1016), (24, 40, 0, 500), (70, 1, 0, 501)],
+                        dtype=torch.int32)
+    attr = torch.tensor([(1, 0, 0), (0, 0, 0), (1, 0, 0), (1, 0, 0)], dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(72, rows, cols, Hkv, D, Hq, wid=49)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == 0
+    compare(out, ref, "two segments per sequence")
+
+
 def test_single_segment_equals_prefill_on_the_column_view():
     say("varlen vs prefill on a strided column")
     rows, cols, Hkv, D, Hq = 4096, 5, 2, 128, 16
