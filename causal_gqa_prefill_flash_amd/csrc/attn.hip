@@ -1855,7 +1855,19 @@ void timing_stop(hipEvent_t start, hipStream_t s) {
 
 struct DeviceInfo {
     int cus;
+    int prefill_per_cu[3];  // resident prefill workgroups per CU at D = 64, 128, 256
 };
+
+// Resident workgroups per CU of a kernel (the occupancy API; 1 if it cannot
+// answer).
+template <class K>
+int resident_per_cu(K kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+        n = 1;
+    (void)hipGetLastError();
+    return n;
+}
 
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -1870,6 +1882,9 @@ int device_info(DeviceInfo* out) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
         g_dev[dev].cus = cus;
+        g_dev[dev].prefill_per_cu[0] = resident_per_cu(prefill_kernel<64>, kThreads);
+        g_dev[dev].prefill_per_cu[1] = resident_per_cu(prefill_kernel<128>, kThreads);
+        g_dev[dev].prefill_per_cu[2] = resident_per_cu(prefill256_kernel, kWaves256 * kWave);
     });
     if (g_dev[dev].cus <= 0) return fail(ATTN_ERR_HIP, "could not read the compute-unit count");
     *out = g_dev[dev];
@@ -1915,9 +1930,11 @@ constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Key splits of a prefill launch: enough workgroups to fill every compute
-// unit (one resident at D=128, two at D=64), with at least 1024 keys per
-// split.
-int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
+// unit once (as many per CU as the occupancy API reports resident for the
+// kernel: one for each head dimension's kernel today), with at least 1024
+// keys per split.
+int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, const DeviceInfo& di) {
+    const int cus = di.cus;
     int forced = env_int("ATTN_FORCE_SPLITS", 0);
     RowMap rm = row_map(Hq / Hkv, D == 256 ? kBM256 : kBM);
     int64_t base = (int64_t)((Lq + rm.P - 1) / rm.P) * rm.hchunks * B * Hkv;
@@ -1927,7 +1944,7 @@ int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, int cus) {
     if (forced > 0) {
         ns = forced;
     } else {
-        const int per_cu = D == 64 ? 2 : 1;
+        const int per_cu = di.prefill_per_cu[D == 64 ? 0 : (D == 128 ? 1 : 2)];
         int64_t want = (per_cu * (int64_t)cus + base - 1) / (base > 0 ? base : 1);
         ns = (int)(want < kMaxSplits ? want : kMaxSplits);
         if (ns > by_keys) ns = by_keys;
@@ -1989,7 +2006,7 @@ size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, in
     if (Lq == 0) return 0;
     DeviceInfo di;
     if (device_info(&di) != ATTN_OK) return 0;
-    return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus));
+    return prefill_ws_bytes(B, Hq, Lq, D, prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di));
 }
 
 // Both prefill entry points: with bounds (device (q_pos0, kv_len)), the
@@ -2030,7 +2047,7 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
 
     DeviceInfo di;
     if ((st = device_info(&di))) return st;
-    const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di.cus);
+    const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di);
     const size_t errb = bounds ? 256 : 0;
     const size_t need = errb + prefill_ws_bytes(B, Hq, Lq, D, nsplit);
     if (need > 0 && (!workspace || ws_bytes < need))
