@@ -1049,8 +1049,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 // hold 128 accumulator and 64 query-fragment registers, so only one wave
 // fits per SIMD.  The workgroup is four waves (128 rows, one wave per SIMD)
 // over 64-key K and V tiles double-buffered in LDS (4 x 32 KB): while the
-// waves compute tile t, the copies of tile t+1 are in flight.  Each tile
-// takes the exact online softmax (running maximum and rescale).
+// waves compute tile t, the copies of tile t+1 are in flight.  The softmax
+// is the fixed-reference pass with an exact rerun, as in the prefill kernel.
 
 constexpr int kWaves256 = 4;
 constexpr int kBM256 = kWaves256 * 32;
@@ -1075,8 +1075,12 @@ __device__ inline void copy_tile256(const u16* base, int64_t rs, int k0, int k_h
 
 // One key tile of the D = 256 loop: copies of the next tile into (Kn, Vn)
 // go out first, then the wave waits for its copies of this tile and the
-// workgroup barrier makes every wave's copies visible; scores, mask, exact
+// workgroup barrier makes every wave's copies visible; scores, mask,
 // softmax, PV; a closing barrier frees (Kc, Vc) for the copies two tiles on.
+// The softmax is that of the prefill kernel: EXACT, against each row's
+// running maximum; otherwise tile 0 sets a fixed reference and later tiles
+// neither take maxima nor rescale (the caller checks the sums).
+template <bool EXACT>
 __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_t vrs, int t,
                                int n, int k_lo, int k_hi, int t_in0, int t_in1,
                                const bf16x8 (*qf)[16], const LaneBounds* lb, float c,
@@ -1093,9 +1097,12 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
     TileScores S;
     qk_tile<D>(Kc, qf, S, NoCopy{}, NoCopy{});
     if (t < t_in0 || t >= t_in1) mask_tile(S, k_lo + t * kBN, lb);
-    float alpha[kNT], lsum[kNT];
-    update_max(S, c, st.m, alpha);
-    rescale<D>(alpha, st);
+    float lsum[kNT];
+    if (EXACT || t == 0) {
+        float alpha[kNT];
+        update_max(S, c, st.m, alpha);
+        rescale<D>(alpha, st);
+    }
     TileP pk;
     softmax_tile(S, c, st.m, pk, lsum);
     st.l[0] += lsum[0];
@@ -1172,14 +1179,34 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         const LaneBounds lb = lane_bounds(k_lo, k_hi, 1, a.window, p_lane);
         const u16* kb = a.k + b * a.ks[0] + hk * a.ks[1];
         const u16* vb = a.v + b * a.vs[0] + hk * a.vs[1];
+        // the fixed-reference pass, then the exact one if a row's sum left
+        // [2^-64, 2^64] (as the prefill kernel)
+        __shared__ int rerun;
+        if (threadIdx.x == 0) rerun = 0;
         copy_tile256(kb, a.ks[2], k_lo, k_hi, sk0);
         copy_tile256(vb, a.vs[2], k_lo, k_hi, sv0);
         for (int t = 0; t < n; t += 2) {
-            tile256(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb, a.c, st,
-                    sk0, sv0, sk1, sv1);
+            tile256<false>(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
+                           a.c, st, sk0, sv0, sk1, sv1);
             if (t + 1 < n)
-                tile256(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
-                        a.c, st, sk1, sv1, sk0, sv0);
+                tile256<false>(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
+                               qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+        }
+        const float lrow = sum_across_halves(st.l[0]);
+        const bool bad = lb.lo < k_hi && !(lrow >= 0x1p-64f && lrow <= 0x1p64f);
+        if (__any(bad) && lane == 0) rerun = 1;
+        __syncthreads();
+        if (rerun) {
+            init_state<D>(st);
+            copy_tile256(kb, a.ks[2], k_lo, k_hi, sk0);
+            copy_tile256(vb, a.vs[2], k_lo, k_hi, sv0);
+            for (int t = 0; t < n; t += 2) {
+                tile256<true>(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf,
+                              &lb, a.c, st, sk0, sv0, sk1, sv1);
+                if (t + 1 < n)
+                    tile256<true>(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
+                                  qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+            }
         }
     }
 
