@@ -518,3 +518,68 @@ def test_kv_write_then_attend_reads_the_written_key():
     stale = oracle.varlen(q[:1], ks, vs, info[:1], seg_attr=torch.tensor([(1, 0, R)],
                                                                       dtype=torch.int32))
     assert not torch.allclose(full, stale)
+
+
+# ------------------------------------------------------- randomised brute force
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as hst  # noqa: E402
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(Hkv=hst.integers(1, 2), g=hst.integers(1, 3), Lq=hst.integers(1, 7),
+       Lkv=hst.integers(0, 9), q_pos0=hst.integers(-4, 10), window=hst.integers(0, 6),
+       D=hst.sampled_from([2, 4, 8]), seed=hst.integers(0, 10 ** 6))
+def test_prefill_vs_brute_random(Hkv, g, Lq, Lkv, q_pos0, window, D, seed):
+    """Random tiny prefill shapes (GQA groups, rows before the first key,
+    windows, no keys): the oracle equals the brute force to 1e-12."""
+    Hq = Hkv * g
+    q = synth.randn_bf16((1, Hq, Lq, D), seed)
+    k = synth.randn_bf16((1, Hkv, Lkv, D), seed + 1)
+    v = synth.randn_bf16((1, Hkv, Lkv, D), seed + 2)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.prefill(q, k, v, scale, q_pos0=q_pos0, window=window)
+    ref = torch.tensor(brute.prefill(_lists(q), _lists(k), _lists(v), scale, q_pos0, window),
+                       dtype=torch.float64).reshape(1, Hq, Lq, D)
+    torch.testing.assert_close(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(data=hst.data())
+def test_varlen_vs_brute_random(data):
+    """Random tiny tables of disjoint segments over a small store: causal or
+    not, windows, ring moduli (wrapped or not), queries before the first key;
+    the oracle equals the brute force to 1e-12 and uncovered rows are zero."""
+    rows = data.draw(hst.integers(2, 10))
+    cols = data.draw(hst.integers(2, 4))
+    Hkv = data.draw(hst.integers(1, 2))
+    Hq = Hkv * data.draw(hst.integers(1, 2))
+    D = data.draw(hst.sampled_from([2, 4]))
+    nseg = data.draw(hst.integers(0, 2 * (cols - 1)))
+    info, attr, t = [], [], 0
+    for _ in range(nseg):
+        t += data.draw(hst.integers(0, 2))
+        q_len = data.draw(hst.integers(0, 4))
+        col = data.draw(hst.integers(0, cols - 2))
+        causal = data.draw(hst.integers(0, 1))
+        ring = data.draw(hst.integers(0, rows))  # 0: flat storage
+        R = ring if ring > 0 else rows
+        kv_end = data.draw(hst.integers(0, 3 * R if ring > 0 else rows))
+        window = data.draw(hst.integers(0, 4))
+        info.append((t, q_len, col, kv_end))
+        attr.append((causal, window, ring))
+        t += q_len
+    T = max(1, t + data.draw(hst.integers(0, 2)))  # the brute force needs one packed row
+    seed = data.draw(hst.integers(0, 10 ** 6))
+    ks = synth.randn_bf16((rows, cols, Hkv, D), seed)
+    vs = synth.randn_bf16((rows, cols, Hkv, D), seed + 1)
+    q = synth.randn_bf16((T, Hq, D), seed + 2)
+    scale = 0.5
+    got, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr or None, scale=scale,
+                               return_flags=True)
+    assert flags == 0
+    ref = brute.varlen(_lists(q), _lists(ks), _lists(vs), info, attr, scale)
+    torch.testing.assert_close(got, torch.tensor(ref, dtype=torch.float64).reshape(T, Hq, D),
+                               rtol=1e-12, atol=1e-12)
