@@ -1281,8 +1281,15 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     int i = (int)(row % a.Lq);
     int h = (int)((row / a.Lq) % a.Hq);
     int b = (int)(row / ((int64_t)a.Lq * a.Hq));
-    combine_row<D>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit, d0,
-                   a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2]);
+    u16* orow = a.out + b * a.os[0] + (int64_t)h * a.os[1] + (int64_t)i * a.os[2];
+    // loads of every split in flight at once, in the narrowest group that
+    // holds them (no clamped duplicates)
+    if (a.nsplit <= 4)
+        combine_row<D, 4>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit,
+                          d0, orow);
+    else
+        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit,
+                          d0, orow);
 }
 
 // ---------------------------------------------------------------- varlen
