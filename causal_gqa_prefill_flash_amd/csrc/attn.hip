@@ -137,38 +137,38 @@ typedef __attribute__((address_space(1))) const void glb_void;
 // Geometry of the global -> LDS tile copies.  Each wave instruction fills
 // 1 KB of LDS: lane l's 16 bytes land at chunk position (instruction * 64 + l),
 // which holds logical chunk (position ^ swz(row)) of its row.  Wave w issues
-// instructions w, w + kWaves, ...
-template <int D>
+// instructions w, w + NW, ...
+template <int D, int NW = kCopyWaves>
 struct CopyPlan {
     static constexpr int CH = D / 8;                // 16-byte chunks per row
     static constexpr int ROWS = 64 / CH;            // rows per wave instruction
     static constexpr int INSTR = kBN / ROWS;        // wave instructions per tensor
-    static constexpr int PER_WAVE = INSTR / kCopyWaves;
+    static constexpr int PER_WAVE = INSTR / NW;
     static __device__ int wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
     static __device__ int row(int i) {
-        return (wave() + i * kCopyWaves) * ROWS + (threadIdx.x & (kWave - 1)) / CH;
+        return (wave() + i * NW) * ROWS + (threadIdx.x & (kWave - 1)) / CH;
     }
     static __device__ int chunk(int i) {
         return ((threadIdx.x & (kWave - 1)) % CH) ^ swz<D>(row(i));
     }
     static __device__ int lds_off(int i) {  // elements
-        return (wave() + i * kCopyWaves) * 512;
+        return (wave() + i * NW) * 512;
     }
 };
 
 // Per-lane byte offsets of this wave's copy instructions inside a tile of
 // consecutive rows (row * stride + chunk), the same for every tile.
-template <int D>
+template <int D, int NW = kCopyWaves>
 struct CopyOffsets {
-    uint32_t o[CopyPlan<D>::PER_WAVE];
+    uint32_t o[CopyPlan<D, NW>::PER_WAVE];
 };
 
-template <int D>
-__device__ inline CopyOffsets<D> copy_offsets(int rs2) {
-    CopyOffsets<D> c;
+template <int D, int NW = kCopyWaves>
+__device__ inline CopyOffsets<D, NW> copy_offsets(int rs2) {
+    typedef CopyPlan<D, NW> CP;
+    CopyOffsets<D, NW> c;
 #pragma unroll
-    for (int i = 0; i < CopyPlan<D>::PER_WAVE; ++i)
-        c.o[i] = (uint32_t)(CopyPlan<D>::row(i) * rs2 + 16 * CopyPlan<D>::chunk(i));
+    for (int i = 0; i < CP::PER_WAVE; ++i) c.o[i] = (uint32_t)(CP::row(i) * rs2 + 16 * CP::chunk(i));
     return c;
 }
 
@@ -186,14 +186,14 @@ struct BufRsrc {  // placeholder: buffer resources exist only in the device pass
 // between MFMAs.  The copy goes through a buffer resource spanning exactly
 // the rows below k_hi: rows past it, and every row of a tile at or past
 // k_hi (whose stage nobody reads), land in LDS as zeros and touch no memory.
-template <int D>
+template <int D, int NW = kCopyWaves>
 struct TileCopyFlat {
-    static constexpr int N = CopyPlan<D>::PER_WAVE;
+    static constexpr int N = CopyPlan<D, NW>::PER_WAVE;
     BufRsrc r;
     u16* dst;
     const uint32_t* o;
     __device__ TileCopyFlat(const KVFlat&, const u16* tb, int64_t rs, int rs2,
-                            const CopyOffsets<D>& co, int k0, int k_hi, u16* d)
+                            const CopyOffsets<D, NW>& co, int k0, int k_hi, u16* d)
         : dst(d), o(co.o) {
         // 32-bit scalar arithmetic, no branches (k0 <= k_hi)
         const int nv = min(k_hi - k0, kBN);
@@ -207,8 +207,8 @@ struct TileCopyFlat {
     }
     __device__ void issue(int i) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + CopyPlan<D>::lds_off(i)), 16,
-                                                 o[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + CopyPlan<D, NW>::lds_off(i)),
+                                                 16, o[i], 0, 0, 0);
 #else
         (void)i;
 #endif
@@ -636,9 +636,10 @@ __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const La
 // in flight (those issued in this phase), then the workgroup barrier.
 template <int NPEND>
 __device__ inline void copy_wait_barrier() {
-    static_assert(NPEND >= 0 && NPEND < 16, "vmcnt field");
+    // vmcnt is 6 bits: 3:0 and 15:14 of the immediate
+    static_assert(NPEND >= 0 && NPEND < 64, "vmcnt field");
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | NPEND);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NPEND & 15) | ((NPEND >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -1055,22 +1056,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 constexpr int kWaves256 = 4;
 constexpr int kBM256 = kWaves256 * 32;
 
-// This wave's share (instructions w, w + 4, ...) of the copy of keys
-// [k0, k0 + 64) of one tensor of flat storage into an LDS tile; rows at or
-// past k_hi repeat row k_hi - 1 (their scores are masked).
-__device__ inline void copy_tile256(const u16* base, int64_t rs, int k0, int k_hi, u16* dst) {
-    constexpr int D = 256, CH = D / 8, ROWS = 64 / CH, INSTR = kBN / ROWS;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = threadIdx.x & (kWave - 1);
+typedef TileCopyFlat<256, kWaves256> Copy256;
+typedef CopyOffsets<256, kWaves256> Offs256;
+
+// This wave's share of the copy of keys [k0, k0 + 64) of one tensor into an
+// LDS tile (zeros for rows at or past k_hi).
+__device__ inline void copy_tile256(const u16* base, int64_t rs, const Offs256& co, int k0,
+                                    int k_hi, u16* dst) {
+    const Copy256 cp(KVFlat{}, base, rs, (int)(rs * 2), co, k0 < k_hi ? k0 : k_hi, k_hi, dst);
 #pragma unroll
-    for (int j = 0; j < INSTR / kWaves256; ++j) {
-        const int i = w + j * kWaves256;
-        const int r = i * ROWS + lane / CH;
-        const int k = min(k0 + r, k_hi - 1);
-        __builtin_amdgcn_global_load_lds(
-            (glb_void*)(base + (int64_t)k * rs + 8 * ((lane % CH) ^ swz<D>(r))),
-            (lds_void*)(dst + i * 512), 16, 0, 0);
-    }
+    for (int i = 0; i < Copy256::N; ++i) cp.issue(i);
 }
 
 // One key tile of the D = 256 loop: copies of the next tile into (Kn, Vn)
@@ -1080,16 +1075,19 @@ __device__ inline void copy_tile256(const u16* base, int64_t rs, int k0, int k_h
 // The softmax is that of the prefill kernel: EXACT, against each row's
 // running maximum; otherwise tile 0 sets a fixed reference and later tiles
 // neither take maxima nor rescale (the caller checks the sums).
-template <bool EXACT>
-__device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_t vrs, int t,
+template <bool EXACT, bool FIRST = false>
+__device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_t vrs,
+                               const Offs256& kco, const Offs256& vco, int t,
                                int n, int k_lo, int k_hi, int t_in0, int t_in1,
                                const bf16x8 (*qf)[16], const LaneBounds* lb, float c,
                                RowState<256>& st, const u16* Kc, const u16* Vc, u16* Kn, u16* Vn) {
     constexpr int D = 256;
     if (t + 1 < n) {
-        copy_tile256(kb, krs, k_lo + (t + 1) * kBN, k_hi, Kn);
-        copy_tile256(vb, vrs, k_lo + (t + 1) * kBN, k_hi, Vn);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (kBN / (64 / (D / 8))) / kWaves256));
+        copy_tile256(kb, krs, kco, k_lo + (t + 1) * kBN, k_hi, Kn);
+        copy_tile256(vb, vrs, vco, k_lo + (t + 1) * kBN, k_hi, Vn);
+        // vmcnt(16): this wave's copies of the next tile stay in flight
+        constexpr int NP = 2 * Copy256::N;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NP & 15) | ((NP >> 4) << 14));
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
     }
@@ -1098,10 +1096,10 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
     qk_tile<D>(Kc, qf, S, NoCopy{}, NoCopy{});
     if (t < t_in0 || t >= t_in1) mask_tile(S, k_lo + t * kBN, lb);
     float lsum[kNT];
-    if (EXACT || t == 0) {
+    if (EXACT || FIRST) {
         float alpha[kNT];
         update_max(S, c, st.m, alpha);
-        rescale<D>(alpha, st);
+        if (!FIRST) rescale<D>(alpha, st);  // tile 0: O and l are still zero
     }
     TileP pk;
     softmax_tile(S, c, st.m, pk, lsum);
@@ -1179,18 +1177,22 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         const LaneBounds lb = lane_bounds(k_lo, k_hi, 1, a.window, p_lane);
         const u16* kb = a.k + b * a.ks[0] + hk * a.ks[1];
         const u16* vb = a.v + b * a.vs[0] + hk * a.vs[1];
+        const Offs256 kco = copy_offsets<D, kWaves256>((int)(a.ks[2] * 2));
+        const Offs256 vco = copy_offsets<D, kWaves256>((int)(a.vs[2] * 2));
         // the fixed-reference pass, then the exact one if a row's sum left
         // [2^-64, 2^64] (as the prefill kernel)
         __shared__ int rerun;
         if (threadIdx.x == 0) rerun = 0;
-        copy_tile256(kb, a.ks[2], k_lo, k_hi, sk0);
-        copy_tile256(vb, a.vs[2], k_lo, k_hi, sv0);
-        for (int t = 0; t < n; t += 2) {
-            tile256<false>(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
-                           a.c, st, sk0, sv0, sk1, sv1);
+        copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
+        copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
+        tile256<false, true>(kb, vb, a.ks[2], a.vs[2], kco, vco, 0, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
+                             a.c, st, sk0, sv0, sk1, sv1);
+        for (int t = 1; t < n; t += 2) {
+            tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
+                           a.c, st, sk1, sv1, sk0, sv0);
             if (t + 1 < n)
-                tile256<false>(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
-                               qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+                tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
+                               qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
         }
         const float lrow = sum_across_halves(st.l[0]);
         const bool bad = lb.lo < k_hi && !(lrow >= 0x1p-64f && lrow <= 0x1p64f);
@@ -1198,13 +1200,13 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         __syncthreads();
         if (rerun) {
             init_state<D>(st);
-            copy_tile256(kb, a.ks[2], k_lo, k_hi, sk0);
-            copy_tile256(vb, a.vs[2], k_lo, k_hi, sv0);
+            copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
+            copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
             for (int t = 0; t < n; t += 2) {
-                tile256<true>(kb, vb, a.ks[2], a.vs[2], t, n, k_lo, k_hi, (int)t0, (int)t1, qf,
+                tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1, qf,
                               &lb, a.c, st, sk0, sv0, sk1, sv1);
                 if (t + 1 < n)
-                    tile256<true>(kb, vb, a.ks[2], a.vs[2], t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
+                    tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
                                   qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
             }
         }
