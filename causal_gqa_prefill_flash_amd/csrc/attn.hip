@@ -1068,10 +1068,12 @@ __device__ inline void copy_tile256(const u16* base, int64_t rs, const Offs256& 
     for (int i = 0; i < Copy256::N; ++i) cp.issue(i);
 }
 
-// One key tile of the D = 256 loop: copies of the next tile into (Kn, Vn)
-// go out first, then the wave waits for its copies of this tile and the
-// workgroup barrier makes every wave's copies visible; scores, mask,
-// softmax, PV; a closing barrier frees (Kc, Vc) for the copies two tiles on.
+// One key tile of the D = 256 loop.  The wave waits for its copies of this
+// tile, and the workgroup barrier makes every wave's copies visible and
+// tells that every wave is done with the previous tile's stages (Kn, Vn);
+// the copies of the next tile into them are spread between the MFMAs of the
+// scores, then mask, softmax, PV.  (Issued before the barrier instead, the
+// copies made the compiler wait for the K copy before the first K read.)
 // The softmax is that of the prefill kernel: EXACT, against each row's
 // running maximum; otherwise tile 0 sets a fixed reference and later tiles
 // neither take maxima nor rescale (the caller checks the sums).
@@ -1082,18 +1084,14 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
                                const bf16x8 (*qf)[16], const LaneBounds* lb, float c,
                                RowState<256>& st, const u16* Kc, const u16* Vc, u16* Kn, u16* Vn) {
     constexpr int D = 256;
-    if (t + 1 < n) {
-        copy_tile256(kb, krs, kco, k_lo + (t + 1) * kBN, k_hi, Kn);
-        copy_tile256(vb, vrs, vco, k_lo + (t + 1) * kBN, k_hi, Vn);
-        // vmcnt(16): this wave's copies of the next tile stay in flight
-        constexpr int NP = 2 * Copy256::N;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NP & 15) | ((NP >> 4) << 14));
-    } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __builtin_amdgcn_s_barrier();
+    // past the range: zeros into stages nobody reads, no memory touched
+    const int k1 = t + 1 < n ? k_lo + (t + 1) * kBN : k_hi;
+    const Copy256 ck(KVFlat{}, kb, krs, (int)(krs * 2), kco, k1, k_hi, Kn);
+    const Copy256 cv(KVFlat{}, vb, vrs, (int)(vrs * 2), vco, k1, k_hi, Vn);
     TileScores S;
-    qk_tile<D>(Kc, qf, S, NoCopy{}, NoCopy{});
+    qk_tile<D>(Kc, qf, S, ck, cv);
     if (t < t_in0 || t >= t_in1) mask_tile(S, k_lo + t * kBN, lb);
     float lsum[kNT];
     if (EXACT || FIRST) {
@@ -1105,7 +1103,6 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
     softmax_tile(S, c, st.m, pk, lsum);
     st.l[0] += lsum[0];
     pv_tile<D>(Vc, pk, st, NoCopy{});
-    __builtin_amdgcn_s_barrier();
 }
 
 __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(PrefillArgs a) {
@@ -1185,15 +1182,16 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         if (threadIdx.x == 0) rerun = 0;
         copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
         copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
-        tile256<false, true>(kb, vb, a.ks[2], a.vs[2], kco, vco, 0, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
-                             a.c, st, sk0, sv0, sk1, sv1);
+        tile256<false, true>(kb, vb, a.ks[2], a.vs[2], kco, vco, 0, n, k_lo, k_hi, (int)t0,
+                             (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
         for (int t = 1; t < n; t += 2) {
-            tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1, qf, &lb,
-                           a.c, st, sk1, sv1, sk0, sv0);
+            tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1,
+                           qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
             if (t + 1 < n)
-                tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
-                               qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
+                tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0,
+                               (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the last tile's (empty) copies
         const float lrow = sum_across_halves(st.l[0]);
         const bool bad = lb.lo < k_hi && !(lrow >= 0x1p-64f && lrow <= 0x1p64f);
         if (__any(bad) && lane == 0) rerun = 1;
@@ -1203,12 +1201,13 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
             copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
             copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
             for (int t = 0; t < n; t += 2) {
-                tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1, qf,
-                              &lb, a.c, st, sk0, sv0, sk1, sv1);
+                tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0,
+                              (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
                 if (t + 1 < n)
-                    tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0, (int)t1,
-                                  qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+                    tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi,
+                                  (int)t0, (int)t1, qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
             }
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
     }
 
