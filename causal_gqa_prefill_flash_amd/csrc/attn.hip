@@ -33,6 +33,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -102,6 +103,14 @@ struct KVFlat {
     __device__ int advance(int base, int off) const { return base + off; }
 };
 
+// n mod R for n < 2^31, R >= 1, with magic = (2^32 - 1) / R: the quotient
+// estimate umulhi(n, magic) is the true quotient or one less, so one
+// conditional subtraction finishes (no division instruction).
+__device__ inline unsigned mod_magic(unsigned n, unsigned R, unsigned magic) {
+    const unsigned r = n - __umulhi(n, magic) * R;
+    return r >= R ? r - R : r;
+}
+
 // Key/value rows of one column of a [rows, cols, H, D] store; position k
 // lives at row k mod R.
 struct KVRing {
@@ -109,6 +118,7 @@ struct KVRing {
     const u16* vb;
     int64_t ks, vs;
     int R;
+    unsigned magic;  // (2^32 - 1) / R, for mod_magic
     __device__ int row(int j) const { return j % R; }
     __device__ bool contiguous(int j, int n) const { return j % R + n <= R; }
     __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
@@ -172,6 +182,17 @@ __device__ inline CopyOffsets<D, NW> copy_offsets(int rs2) {
     return c;
 }
 
+// r mod R for the rows r of this wave's copy instructions inside a tile
+// (ring storage of R rows).
+template <int D>
+__device__ inline CopyOffsets<D> ring_offsets(int R) {
+    CopyOffsets<D> c;
+#pragma unroll
+    for (int i = 0; i < CopyPlan<D>::PER_WAVE; ++i)
+        c.o[i] = (uint32_t)CopyPlan<D>::row(i) % (uint32_t)R;
+    return c;
+}
+
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 #else
@@ -218,23 +239,30 @@ struct TileCopyFlat {
 // The same for one column of ring storage: each lane addresses its own row
 // (position mod R), so a tile may wrap the ring.  Rows past k_hi repeat row
 // k_hi - 1, and a tile at or past k_hi copies row k_hi - 1 throughout.
+//   The store row of key kc + r is (kc mod R + r mod R) mod R: kc mod R and
+//   (for the clamped rows) last mod R are uniform, taken once per tile with
+//   mod_magic; r mod R of this lane's copy rows comes in `co` (ring_offsets),
+//   so each copy adds and subtracts R at most once, with no division.
 template <int D>
 struct TileCopyRing {
     static constexpr int N = CopyPlan<D>::PER_WAVE;
     const u16* tb;
     int64_t rs;
-    int R, kc, last;
+    int R, base, last, lastm;
+    const uint32_t* o;
     u16* dst;
-    __device__ TileCopyRing(const KVRing& kv, const u16* t, int64_t s, int, const CopyOffsets<D>&,
+    __device__ TileCopyRing(const KVRing& kv, const u16* t, int64_t s, int, const CopyOffsets<D>& co,
                             int k0, int k_hi, u16* d)
-        : tb(t), rs(s), R(kv.R), dst(d) {
-        kc = k0 < k_hi ? k0 : k_hi - 1;
+        : tb(t), rs(s), R(kv.R), o(co.o), dst(d) {
+        const int kc = k0 < k_hi ? k0 : k_hi - 1;
         last = k_hi - 1 - kc;
+        base = (int)mod_magic((unsigned)kc, (unsigned)R, kv.magic);
+        lastm = (int)mod_magic((unsigned)last, (unsigned)R, kv.magic);
     }
     __device__ void issue(int i) const {
         const int r = CopyPlan<D>::row(i);
-        const unsigned pos = (unsigned)(kc + (r < last ? r : last));
-        const unsigned row = pos % (unsigned)R;
+        unsigned row = (unsigned)base + (r < last ? o[i] : (unsigned)lastm);
+        row = row >= (unsigned)R ? row - (unsigned)R : row;
         __builtin_amdgcn_global_load_lds(
             (glb_void*)(tb + (int64_t)row * rs + 8 * CopyPlan<D>::chunk(i)),
             (lds_void*)(dst + CopyPlan<D>::lds_off(i)), 16, 0, 0);
@@ -709,8 +737,13 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     L.k_hi = k_hi;
     L.ks2 = (int)(kv.ks * 2);  // below 2^25 (host check) for flat storage
     L.vs2 = (int)(kv.vs * 2);
-    L.kco = copy_offsets<D>(L.ks2);
-    L.vco = copy_offsets<D>(L.vs2);
+    if constexpr (std::is_same<KV, KVRing>::value) {
+        L.kco = ring_offsets<D>(kv.R);
+        L.vco = L.kco;
+    } else {
+        L.kco = copy_offsets<D>(L.ks2);
+        L.vco = copy_offsets<D>(L.vs2);
+    }
     interior_tiles<D>(L, causal, window, p_min, p_max);
     const int n = (k_hi - k_lo + kBN - 1) / kBN;
     L.n = n;
@@ -1528,7 +1561,7 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
     load_q<D>(qf[0], a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid, a.negate);
     const KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
                     a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0],
-                    sg.R};
+                    sg.R, 0xFFFFFFFFu / (unsigned)sg.R};
     const LaneBounds lb = lane_bounds(k_lo, k_hi, sg.causal, sg.window, p_lane);
     RowState<D> st;
     init_state<D>(st);
@@ -1685,7 +1718,8 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     RowState<D> st;
     init_state<D>(st);
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
-              a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R};
+              a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R,
+              0xFFFFFFFFu / (unsigned)sg.R};
     attend<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
 #pragma unroll

@@ -244,3 +244,21 @@ def test_call_level_modes_without_seg_attr():
     out2, _ = _gpu_varlen(q, ks, vs, info, causal=0)
     ref2 = oracle.varlen(q, ks, vs, info, causal=0)
     compare(out2, ref2, "call-level non-causal")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_rings_wrap_inside_a_tile(D):
+    """Ring storage of fewer rows than a 64-key tile (5, 37, 63) and around it
+    (64, 65): one tile's keys wrap the ring several times; compute-path and
+    decode-path segments, each window no longer than its ring."""
+    say("varlen small rings D=%d" % D)
+    rows, cols, Hkv, Hq = 200, 6, 2, 8
+    info = torch.tensor([(0, 20, 0, 300), (24, 3, 1, 500), (30, 10, 2, 129),
+                         (45, 8, 3, 1000), (60, 2, 4, 777)], dtype=torch.int32)
+    attr = torch.tensor([(1, 37, 37), (1, 5, 5), (1, 63, 63), (1, 64, 64), (1, 65, 65)],
+                        dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(70, rows, cols, Hkv, D, Hq, wid=46)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == 0
+    compare(out, ref, "small rings")
