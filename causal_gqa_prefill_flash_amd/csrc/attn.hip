@@ -1502,7 +1502,7 @@ __device__ inline void load_k_regs(bf16x8 (&kr)[2][D / 16], const KVRing& kv, in
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int k = min(k0 + 32 * t + (lane & 31), k_hi - 1);
-        const u16* row = kv.krow_at((int)((unsigned)k % (unsigned)kv.R));
+        const u16* row = kv.krow_at((int)mod_magic((unsigned)k, (unsigned)kv.R, kv.magic));
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             kr[t][kk] = __builtin_bit_cast(bf16x8, ld16(row + 16 * kk + 8 * hh));
@@ -1520,7 +1520,7 @@ __device__ inline void copy_v_wave(const KVRing& kv, int k0, int k_hi, u16* dst)
     for (int i = 0; i < INSTR; ++i) {
         const int r = i * ROWS + lane / CH;
         const int k = min(k0 + r, k_hi - 1);
-        const int row = (int)((unsigned)k % (unsigned)kv.R);
+        const int row = (int)mod_magic((unsigned)k, (unsigned)kv.R, kv.magic);
         __builtin_amdgcn_global_load_lds(
             (glb_void*)(kv.vb + (int64_t)row * kv.vs + 8 * ((lane % CH) ^ swz<D>(r))),
             (lds_void*)(dst + i * 512), 16, 0, 0);
