@@ -93,14 +93,7 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 struct KVFlat {
     const u16* kb;
     const u16* vb;
-    int64_t ks, vs;
-    __device__ int row(int j) const { return j; }
-    // rows of keys j .. j + n - 1 are consecutive store rows
-    __device__ bool contiguous(int j, int n) const { return true; }
-    __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
-    __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
-    // store row of key k0 + off, given base = row(k0)
-    __device__ int advance(int base, int off) const { return base + off; }
+    int64_t ks, vs;  // row strides in elements
 };
 
 // n mod R for n < 2^31, R >= 1, with magic = (2^32 - 1) / R: the quotient
@@ -119,15 +112,7 @@ struct KVRing {
     int64_t ks, vs;
     int R;
     unsigned magic;  // (2^32 - 1) / R, for mod_magic
-    __device__ int row(int j) const { return j % R; }
-    __device__ bool contiguous(int j, int n) const { return j % R + n <= R; }
     __device__ const u16* krow_at(int r) const { return kb + (int64_t)r * ks; }
-    __device__ const u16* vrow_at(int r) const { return vb + (int64_t)r * vs; }
-    __device__ int advance(int base, int off) const {
-        int r = base + off;
-        while (r >= R) r -= R;
-        return r;
-    }
 };
 
 // LDS tiles hold K and V in their natural [key][d] order, 16-byte chunks of
