@@ -202,7 +202,7 @@ def time_graph(fns, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def cpu_baseline_prefill(q, k, v, w, budget_s=12.0):
+def cpu_baseline_prefill(q, k, v, w, budget_s=30.0):
     """The oracle, as it stands, on a bounded sample of query rows."""
     import oracle
     B, Hq, Lq, D = q.shape
