@@ -32,6 +32,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 #include <utility>
@@ -335,9 +336,22 @@ __device__ inline float sum_across_halves(float x) {
 template <int D>
 struct RowState {
     f32x16 o[kNT][D / 32];  // O^T accumulators: d = 32*dt + 8*(r/4) + 4*(lane/32) + r%4
-    float m[kNT];           // running maximum of raw scores (-inf: nothing seen)
+    float m[kNT];           // running maximum of the scores (-inf: nothing seen)
     float l[kNT];           // this lane's share of the running sum
+    f32x16 mneg[kNT];       // -(fixed reference) in every element: the scores' initial value
 };
+
+// After the tile that fixes the references: the score MFMAs of later tiles
+// start from -m (0 for a row that has seen nothing), so they yield s - m.
+template <int D>
+__device__ inline void set_reference(RowState<D>& st) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float v = st.m[nt] == -INFINITY ? 0.f : -st.m[nt];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.mneg[nt][r] = v;
+    }
+}
 
 // Visible keys of one row inside the range [k_lo, k_hi): the interval
 // lo .. lo + span, in int32.
@@ -369,13 +383,15 @@ typedef f32x16 TileScores[kNT][2];
 // S^T = K Q^T for one key tile (keys in LDS).  Each K fragment read from LDS
 // feeds the MFMAs of all kNT row tiles.  The copy instructions of c1 and c2
 // are spread between the MFMAs.
-template <int D, class C1, class C2>
+// PRE: the accumulators start from init (the negated fixed references), so
+// the tile comes out as s - m.
+template <int D, class C1, class C2, bool PRE = false>
 __device__ inline void qk_tile(const u16* Ks, const bf16x8 (*qf)[D / 16], TileScores& s,
-                               const C1& c1, const C2& c2) {
+                               const C1& c1, const C2& c2, const f32x16* init = nullptr) {
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int NR = 2 * (D / 16), NM = 2 * kNT * (D / 16), NC = C1::N + C2::N;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) s[nt][0] = s[nt][1] = f32x16{};
+    for (int nt = 0; nt < kNT; ++nt) s[nt][0] = s[nt][1] = PRE ? init[nt] : f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         const bf16x8 a0 = k_frag<D>(Ks, 0, kk, lane), a1 = k_frag<D>(Ks, 1, kk, lane);
@@ -451,6 +467,9 @@ __device__ inline void update_max(const TileScores& s, float c, float* m, float*
 // and c > 0, so they give exactly 0.
 typedef uint32_t TileP[kNT][2][8];
 
+// PRE: s already holds s - m (qk_tile from the negated references), and
+// c = 1, so P = 2^s.
+template <bool PRE = false>
 __device__ inline void softmax_tile(const TileScores& s, float c, const float* m, TileP& pk,
                                     float* lsum) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -462,8 +481,9 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float x0 = __builtin_amdgcn_exp2f(fmaf(s[nt][t][r], c, -mc));
-                const float x1 = __builtin_amdgcn_exp2f(fmaf(s[nt][t][r + 1], c, -mc));
+                const float x0 = __builtin_amdgcn_exp2f(PRE ? s[nt][t][r] : fmaf(s[nt][t][r], c, -mc));
+                const float x1 =
+                    __builtin_amdgcn_exp2f(PRE ? s[nt][t][r + 1] : fmaf(s[nt][t][r + 1], c, -mc));
                 const uint32_t w = pack_bf16x2(x0, x1);
                 pk[nt][t][r >> 1] = w;
                 ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
@@ -612,7 +632,7 @@ __device__ inline void pin_v_outputs(TileP& pk, RowState<D>& st) {
 // in Ks), with this wave's copies of a later K tile (ck) spread through the
 // PV product and of a later V tile (cv) through the scores.  No VALU work,
 // so the MFMAs issue back to back.
-template <int D, bool QK, bool PV, class CK, class CV>
+template <int D, bool QK, bool PV, bool PRE, class CK, class CV>
 __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[D / 16],
                                TileScores& S, const TileP& pk, RowState<D>& st, const CK& ck,
                                const CV& cv) {
@@ -620,7 +640,7 @@ __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[
     // separate scheduling regions: keeps the fragment prefetch of the two
     // products from piling up in registers
     if (PV && QK) __builtin_amdgcn_sched_barrier(0);
-    if (QK) qk_tile<D>(Ks, qf, S, cv, NoCopy{});
+    if (QK) qk_tile<D, CV, NoCopy, PRE>(Ks, qf, S, cv, NoCopy{}, st.mneg);
     pin_m_outputs<D>(S, st, QK, PV);
 }
 
@@ -629,7 +649,7 @@ __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[
 // and l when it moves.  Otherwise against the row's fixed reference st.m (0
 // while it is -inf), with no maxima and no rescale; the caller checks
 // afterwards that every row's sum stayed in range.
-template <int D, bool EXACT, class KV>
+template <int D, bool EXACT, bool PRE, class KV>
 __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const LaneBounds* lb,
                                TileScores& S, TileP& pk, RowState<D>& st) {
     if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
@@ -639,7 +659,7 @@ __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const La
         rescale<D>(alpha, st);
     }
     float lsum[kNT];
-    softmax_tile(S, c, st.m, pk, lsum);
+    softmax_tile<PRE>(S, c, st.m, pk, lsum);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) st.l[nt] += lsum[nt];
     pin_v_outputs<D>(pk, st);
@@ -676,16 +696,16 @@ __device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L,
 // softmax phase also prepares the next step's copy descriptors (K(k+3) into
 // Kn, V(k+2) into Vn): scalar work that would otherwise delay the first
 // MFMA of the next phase.
-template <int D, bool EXACT, class KV>
+template <int D, bool EXACT, bool PRE, class KV>
 __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
                                float c, const LaneBounds* lb, TileScores& S, TileP& pk,
                                RowState<D>& st, const u16* Kr, const u16* Vr,
                                typename TileCopySel<D, KV>::T& ck,
                                typename TileCopySel<D, KV>::T& cv, u16* Kn, u16* Vn) {
     typedef typename TileCopySel<D, KV>::T TC;
-    m_phase<D, true, true>(Kr, Vr, qf, S, pk, st, ck, cv);
+    m_phase<D, true, true, PRE>(Kr, Vr, qf, S, pk, st, ck, cv);
     copy_wait_barrier<2 * TC::N>();
-    v_phase<D, EXACT>(L, k, c, lb, S, pk, st);
+    v_phase<D, EXACT, PRE>(L, k, c, lb, S, pk, st);
     ck = k_copy<D>(L, k + 3, Kn);
     cv = v_copy<D>(L, k + 2, Vn);
     phase_barrier();
@@ -709,7 +729,7 @@ __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf
 //   p_lane[nt]: position of this lane's row in row tile nt; p_min/p_max:
 //   extreme positions of the workgroup's rows (for the per-tile mask
 //   decision).
-template <int D, bool EXACT, class KV>
+template <int D, bool EXACT, bool PRE, class KV>
 __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
                              const int64_t* p_lane, int64_t p_min, int64_t p_max,
                              const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
@@ -756,7 +776,8 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     qk_tile<D>(sm.k[0], qf, S, ck, cv);
     pin_m_outputs<D>(S, st, true, false);
     copy_wait_barrier<2 * TC::N>();
-    v_phase<D, true>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
+    v_phase<D, true, false>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
+    if (PRE) set_reference<D>(st);
     ck = k_copy<D>(L, 3, sm.k[0]);
     cv = v_copy<D>(L, 2, sm.v[2]);
     phase_barrier();
@@ -764,18 +785,18 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     for (; k + 2 < n; k += 3) {
         // k = 1 mod 3: K(k) in stage 1, V(k-1) in stage 0; copies of K(k+2) -> 0,
         // V(k+1) -> 2 (ck, cv); the next step's go to K stage 1, V stage 0
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
-        pp_step<D, EXACT>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
+        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
+        pp_step<D, EXACT, PRE>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
                           sm.v[1]);
-        pp_step<D, EXACT>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck, cv, sm.k[0],
+        pp_step<D, EXACT, PRE>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck, cv, sm.k[0],
                           sm.v[2]);
     }
     if (k < n) {
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
+        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
         ++k;
     }
     if (k < n) {
-        pp_step<D, EXACT>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
+        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
                           sm.v[1]);
         ++k;
     }
@@ -792,20 +813,25 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     if (!g1) phase_barrier();  // matches group 1's extra barrier
 }
 
-// Q fragments of one row (zeros for rows that do not exist); the sign of a
-// negative scale is folded into Q, which is exact.
-template <int D>
-__device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, bool negate) {
+// Q fragments of one row, zeros for rows that do not exist.  cq is the
+// softmax scale times log2 e, sign included.  PS: Q times cq, rounded to
+// bf16, so that the scores come out of the MFMAs in log2 units and the
+// softmax takes c = 1.  Otherwise only the sign of cq is folded into Q
+// (exact) and the softmax multiplies by c = |cq|.
+template <int D, bool PS>
+__device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, float cq) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    const uint32_t flip = negate ? 0x80008000u : 0u;
+    const uint32_t flip = cq < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        uint4 u = valid ? ld16(qrow + 16 * kk + 8 * hh) : make_uint4(0, 0, 0, 0);
-        u.x ^= flip;
-        u.y ^= flip;
-        u.z ^= flip;
-        u.w ^= flip;
-        qf[kk] = __builtin_bit_cast(bf16x8, u);
+        const uint4 u = valid ? ld16(qrow + 16 * kk + 8 * hh) : make_uint4(0, 0, 0, 0);
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // bf16 pair: element 0 in the low half
+            w[j] = PS ? pack_bf16x2(__uint_as_float(w[j] << 16) * cq,
+                                    __uint_as_float(w[j] & 0xffff0000u) * cq)
+                      : w[j] ^ flip;
+        qf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
 
@@ -857,6 +883,7 @@ __device__ inline void init_state(RowState<D>& st) {
         for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] = f32x16{};
         st.m[nt] = -INFINITY;
         st.l[nt] = 0.f;
+        st.mneg[nt] = f32x16{};
     }
 }
 
@@ -879,13 +906,17 @@ __device__ inline void split_range(int lo_all, int hi_all, int split, int nsplit
 // checks that its sum lies in [2^-64, 2^64] (which bounds each P of the
 // row); if any row of the workgroup fails, the workgroup redoes the range
 // with the exact running-maximum pass.
-template <int D, class KV>
+//   PS: Q carries the scale (load_q<D, true>) and c = 1; the fixed-reference
+//   pass then starts its score MFMAs from the negated references
+//   (set_reference) and takes 2^s directly.
+template <int D, bool PS, class KV>
 __device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
                        const int64_t* p_lane, int64_t p_min, int64_t p_max,
                        const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
                        const TileSmem<D>& sm) {
     if (threadIdx.x == 0) *sm.rerun = 0;
-    attend_range<D, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st, sm);
+    attend_range<D, false, PS>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
+                               sm);
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -897,8 +928,8 @@ __device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
     __syncthreads();
     if (*sm.rerun) {
         init_state<D>(st);
-        attend_range<D, true>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
-                              sm);
+        attend_range<D, true, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c,
+                                     st, sm);
     }
 }
 
@@ -982,7 +1013,8 @@ __device__ inline int xcd_remap(int L, int N) {
     __shared__ int rerun_flag;                                                           \
     const TileSmem<D> sm{{sk0, sk1, sk2}, {sv0, sv1, sv2}, &rerun_flag}
 
-template <int D>
+// PS: Q carries the scale (chosen by the host for |scale| <= 1/sqrt(D)).
+template <int D, bool PS>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     DECLARE_TILE_SMEM(D);
     const ClockMark cm = clock_mark(a.clk);
@@ -1027,9 +1059,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         hrow[nt] = hk * g + hc * rm.Gc + hl;
         valid[nt] = hl < heads_here && irow[nt] < a.Lq;
         p_lane[nt] = valid[nt] ? q_pos0 + irow[nt] : p_max;
-        load_q<D>(qf[nt],
-                  a.q + b * a.qs[0] + (int64_t)hrow[nt] * a.qs[1] + (int64_t)irow[nt] * a.qs[2],
-                  valid[nt], a.negate);
+        load_q<D, PS>(qf[nt],
+                      a.q + b * a.qs[0] + (int64_t)hrow[nt] * a.qs[1] + (int64_t)irow[nt] * a.qs[2],
+                      valid[nt], a.negate ? -a.c : a.c);
     }
 
     // visible keys of the whole workgroup, then this split's share
@@ -1044,7 +1076,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     init_state<D>(st);
     KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
               a.vs[2]};
-    attend<D>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, a.c, st, sm);
+    const float c = PS ? 1.f : a.c;
+    attend<D, PS>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1055,7 +1088,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                          valid[nt]);
         } else {
             const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[nt]) * a.Lq + irow[nt];
-            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
+            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
                              a.part_ml + row * 2, valid[nt]);
         }
     }
@@ -1095,7 +1128,7 @@ __device__ inline void copy_tile256(const u16* base, int64_t rs, const Offs256& 
 // The softmax is that of the prefill kernel: EXACT, against each row's
 // running maximum; otherwise tile 0 sets a fixed reference and later tiles
 // neither take maxima nor rescale (the caller checks the sums).
-template <bool EXACT, bool FIRST = false>
+template <bool EXACT, bool FIRST, bool PS>
 __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_t vrs,
                                const Offs256& kco, const Offs256& vco, int t,
                                int n, int k_lo, int k_hi, int t_in0, int t_in1,
@@ -1108,21 +1141,25 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
     const int k1 = t + 1 < n ? k_lo + (t + 1) * kBN : k_hi;
     const Copy256 ck(KVFlat{}, kb, krs, (int)(krs * 2), kco, k1, k_hi, Kn);
     const Copy256 cv(KVFlat{}, vb, vrs, (int)(vrs * 2), vco, k1, k_hi, Vn);
+    constexpr bool PRE = PS && !EXACT && !FIRST;  // scores come out as s - m
     TileScores S;
-    qk_tile<D>(Kc, qf, S, ck, cv);
+    qk_tile<D, Copy256, Copy256, PRE>(Kc, qf, S, ck, cv, st.mneg);
     if (t < t_in0 || t >= t_in1) mask_tile(S, k_lo + t * kBN, lb);
     float lsum[kNT];
     if (EXACT || FIRST) {
         float alpha[kNT];
         update_max(S, c, st.m, alpha);
         if (!FIRST) rescale<D>(alpha, st);  // tile 0: O and l are still zero
+        if (PS && FIRST && !EXACT) set_reference<D>(st);
     }
     TileP pk;
-    softmax_tile(S, c, st.m, pk, lsum);
+    softmax_tile<PRE>(S, c, st.m, pk, lsum);
     st.l[0] += lsum[0];
     pv_tile<D>(Vc, pk, st, NoCopy{});
 }
 
+// PS: as prefill_kernel.
+template <bool PS>
 __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(PrefillArgs a) {
     constexpr int D = 256;
     __shared__ __attribute__((aligned(1024))) u16 sk0[kBN * D];
@@ -1161,8 +1198,9 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
     const bool valid = hl < heads_here && irow < a.Lq;
     const int64_t p_lane = valid ? q_pos0 + irow : p_max;
     bf16x8 qf[1][D / 16];
-    load_q<D>(qf[0], a.q + b * a.qs[0] + (int64_t)hrow * a.qs[1] + (int64_t)irow * a.qs[2], valid,
-              a.negate);
+    load_q<D, PS>(qf[0], a.q + b * a.qs[0] + (int64_t)hrow * a.qs[1] + (int64_t)irow * a.qs[2],
+                  valid, a.negate ? -a.c : a.c);
+    const float c = PS ? 1.f : a.c;
 
     int64_t lo64 = a.window > 0 ? p_min - a.window + 1 : 0;
     int64_t hi64 = p_max + 1 < Lkv ? p_max + 1 : Lkv;
@@ -1200,14 +1238,14 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         if (threadIdx.x == 0) rerun = 0;
         copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
         copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
-        tile256<false, true>(kb, vb, a.ks[2], a.vs[2], kco, vco, 0, n, k_lo, k_hi, (int)t0,
-                             (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
+        tile256<false, true, PS>(kb, vb, a.ks[2], a.vs[2], kco, vco, 0, n, k_lo, k_hi, (int)t0,
+                             (int)t1, qf, &lb, c, st, sk0, sv0, sk1, sv1);
         for (int t = 1; t < n; t += 2) {
-            tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1,
-                           qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+            tile256<false, false, PS>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0, (int)t1,
+                           qf, &lb, c, st, sk1, sv1, sk0, sv0);
             if (t + 1 < n)
-                tile256<false>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0,
-                               (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
+                tile256<false, false, PS>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi, (int)t0,
+                               (int)t1, qf, &lb, c, st, sk0, sv0, sk1, sv1);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the last tile's (empty) copies
         const float lrow = sum_across_halves(st.l[0]);
@@ -1219,11 +1257,11 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
             copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
             copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
             for (int t = 0; t < n; t += 2) {
-                tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0,
-                              (int)t1, qf, &lb, a.c, st, sk0, sv0, sk1, sv1);
+                tile256<true, false, PS>(kb, vb, a.ks[2], a.vs[2], kco, vco, t, n, k_lo, k_hi, (int)t0,
+                              (int)t1, qf, &lb, c, st, sk0, sv0, sk1, sv1);
                 if (t + 1 < n)
-                    tile256<true>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi,
-                                  (int)t0, (int)t1, qf, &lb, a.c, st, sk1, sv1, sk0, sv0);
+                    tile256<true, false, PS>(kb, vb, a.ks[2], a.vs[2], kco, vco, t + 1, n, k_lo, k_hi,
+                                  (int)t0, (int)t1, qf, &lb, c, st, sk1, sv1, sk0, sv0);
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
@@ -1236,7 +1274,7 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
     } else {
         const int64_t row =
             (((int64_t)split * a.B + b) * a.Hq + hrow) * a.Lq + irow;
-        store_partial<D>(st.o[0], st.m[0], st.l[0], a.c, a.part_o + row * D, a.part_ml + row * 2,
+        store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 2,
                          valid);
     }
     clock_add(a.clk, cm);
@@ -1543,7 +1581,9 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
     split_range((int)lo64, (int)hi64, split, nsplit, &k_lo, &k_hi);
 
     bf16x8 qf[1][D / 16];
-    load_q<D>(qf[0], a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid, a.negate);
+    load_q<D, false>(qf[0], a.q + (int64_t)t * a.qs[0] + (int64_t)h * a.qs[1], valid,
+                     a.negate ? -a.c : a.c);
+    const float c = a.c;
     const KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
                     a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0],
                     sg.R, 0xFFFFFFFFu / (unsigned)sg.R};
@@ -1566,10 +1606,10 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
         }
         mask_tile(S, k0, &lb);
         float alpha[1], lsum[1];
-        update_max(S, a.c, st.m, alpha);
+        update_max(S, c, st.m, alpha);
         rescale<D>(alpha, st);
         TileP pk;
-        softmax_tile(S, a.c, st.m, pk, lsum);
+        softmax_tile(S, c, st.m, pk, lsum);
         st.l[0] += lsum[0];
         pv_tile<D>(vbuf, pk, st, NoCopy{});
     }
@@ -1590,9 +1630,9 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
         const float mv = sh_m[v][r];
-        L += mv == -INFINITY ? 0.f : sh_l[v][r] * __builtin_amdgcn_exp2f((mv - mref) * a.c);
+        L += mv == -INFINITY ? 0.f : sh_l[v][r] * __builtin_amdgcn_exp2f((mv - mref) * c);
     }
-    const float fw = st.m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[0] - mref) * a.c);
+    const float fw = st.m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[0] - mref) * c);
     float* ob = reinterpret_cast<float*>(vbuf);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -1631,7 +1671,7 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
             *reinterpret_cast<float4*>(po + d) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
         }
         if (w == 0 && hh == 0) {
-            a.part_ml[row * 2] = L > 0.f ? mref * a.c : -INFINITY;
+            a.part_ml[row * 2] = L > 0.f ? mref * c : -INFINITY;
             a.part_ml[row * 2 + 1] = L;
         }
     }
@@ -1692,9 +1732,10 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
         hrow[nt] = hk * g + hc * rm.Gc + hl;
         valid[nt] = hl < heads_here && jrow[nt] < sg.q_len;
         p_lane[nt] = valid[nt] ? base + jrow[nt] : p_max;
-        load_q<D>(qf[nt],
-                  a.q + (int64_t)(sg.q_start + jrow[nt]) * a.qs[0] + (int64_t)hrow[nt] * a.qs[1],
-                  valid[nt], a.negate);
+        load_q<D, false>(qf[nt],
+                         a.q + (int64_t)(sg.q_start + jrow[nt]) * a.qs[0] +
+                             (int64_t)hrow[nt] * a.qs[1],
+                         valid[nt], a.negate ? -a.c : a.c);
     }
 
     int k_lo, k_hi;
@@ -1705,7 +1746,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
               a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R,
               0xFFFFFFFFu / (unsigned)sg.R};
-    attend<D>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
+    attend<D, false>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1936,9 +1977,15 @@ int device_info(DeviceInfo* out) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
         g_dev[dev].cus = cus;
-        g_dev[dev].prefill_per_cu[0] = resident_per_cu(prefill_kernel<64>, kThreads);
-        g_dev[dev].prefill_per_cu[1] = resident_per_cu(prefill_kernel<128>, kThreads);
-        g_dev[dev].prefill_per_cu[2] = resident_per_cu(prefill256_kernel, kWaves256 * kWave);
+        // the fewer of the two variants' (scale in Q or not)
+        g_dev[dev].prefill_per_cu[0] = std::min(resident_per_cu(prefill_kernel<64, true>, kThreads),
+                                                resident_per_cu(prefill_kernel<64, false>, kThreads));
+        g_dev[dev].prefill_per_cu[1] =
+            std::min(resident_per_cu(prefill_kernel<128, true>, kThreads),
+                     resident_per_cu(prefill_kernel<128, false>, kThreads));
+        g_dev[dev].prefill_per_cu[2] =
+            std::min(resident_per_cu(prefill256_kernel<true>, kWaves256 * kWave),
+                     resident_per_cu(prefill256_kernel<false>, kWaves256 * kWave));
     });
     if (g_dev[dev].cus <= 0) return fail(ATTN_ERR_HIP, "could not read the compute-unit count");
     *out = g_dev[dev];
@@ -2149,13 +2196,29 @@ int prefill_call(const void* q, const void* k, const void* v, void* out, int B, 
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)nwg);
     a.clk = timing_clock();
+    // The scale goes into Q (rounded to bf16 with it) when |scale| <= 1/sqrt(D),
+    // the standard scale and below: there that rounding moves the scores by
+    // no more than it does at the standard scale.  A larger scale sharpens
+    // the softmax and would magnify it, so Q stays exact and the softmax
+    // multiplies by the scale in fp32.
+    const bool ps = fabsf(scale) * sqrtf((float)D) <= 1.0001f;
     hipEvent_t t0 = timing_start(s);
-    if (D == 64)
-        hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(kThreads), 0, s, a);
-    else if (D == 128)
-        hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(prefill256_kernel, grid, dim3(kWaves256 * kWave), 0, s, a);
+    if (D == 64) {
+        if (ps)
+            hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+    } else if (D == 128) {
+        if (ps)
+            hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+    } else {
+        if (ps)
+            hipLaunchKernelGGL(prefill256_kernel<true>, grid, dim3(kWaves256 * kWave), 0, s, a);
+        else
+            hipLaunchKernelGGL(prefill256_kernel<false>, grid, dim3(kWaves256 * kWave), 0, s, a);
+    }
     timing_stop(t0, s);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed");
     if (nsplit > 1) {
