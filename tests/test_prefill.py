@@ -73,6 +73,23 @@ def test_scale_sign_and_zero(scale):
     compare(out, ref, "scale %g" % scale)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("mult", [1.0, -1.0, 1.01, -2.0])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_both_scale_paths(D, mult, splits, monkeypatch):
+    """|scale| <= 1/sqrt(D) runs the kernel that carries the scale in Q and
+    starts the scores from the negated references; a larger |scale| runs the
+    one that keeps Q exact.  Both, with either sign, split or not, with a
+    window and edge tiles, against the oracle."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
+    scale = mult / math.sqrt(D)
+    say("scale paths D=%d scale=%g splits=%d" % (D, scale, splits))
+    q, k, v = synth.prefill_inputs(1, 8, 2, 150, 1300, D, wid=24)
+    out = _run(q, k, v, scale=scale, window=700)
+    ref = oracle.prefill(q, k, v, scale, window=700)
+    compare(out, ref, "scale %g D %d splits %d" % (scale, D, splits))
+
+
 def test_output_through_real_strides_and_canary():
     B, Hq, Hkv, Lq, Lkv, D = 2, 8, 2, 90, 600, 128
     say("strided outputs")
