@@ -271,7 +271,8 @@ def bench_prefill(args, name):
             {"bound": "mfma", "achieved": round(ktflops, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(ktflops / PEAK_BF16_TFLOPS, 4),
              "traffic": traffic_from_profile(name),
-             "kernel": "prefill_kernel<%d>" % D if D != 256 else "prefill256_kernel",
+             # the standard scale 1/sqrt(D): the variant that carries the scale in Q
+             "kernel": "prefill_kernel<%d, true>" % D if D != 256 else "prefill256_kernel<true>",
              "kernel_ms_per_launch": round(kms, 4),
              "algorithmic_flop_per_launch": flops,
              "timed": "attention kernel alone: HIP events recorded by the library on "
