@@ -463,8 +463,9 @@ __device__ inline void update_max(const TileScores& s, float c, float* m, float*
 }
 
 // P = 2^(s c - m c) rounded to packed bf16 pairs (the B operand of the PV
-// MFMA); the row sums come from the rounded values.  Masked scores are -inf
-// and c > 0, so they give exactly 0.
+// MFMA), and the row sums of P before rounding.  Masked scores are -inf and
+// c > 0, so they give exactly 0.  The sums use plain adds: the packed dot
+// product would wait on the matrix core while the partner wave's MFMAs run.
 typedef uint32_t TileP[kNT][2][8];
 
 // PRE: s already holds s - m (qk_tile from the negated references), and
@@ -472,7 +473,6 @@ typedef uint32_t TileP[kNT][2][8];
 template <bool PRE = false>
 __device__ inline void softmax_tile(const TileScores& s, float c, const float* m, TileP& pk,
                                     float* lsum) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const float mc = (m[nt] == -INFINITY ? 0.f : m[nt]) * c;  // reference 0 before any key
@@ -484,10 +484,9 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
                 const float x0 = __builtin_amdgcn_exp2f(PRE ? s[nt][t][r] : fmaf(s[nt][t][r], c, -mc));
                 const float x1 =
                     __builtin_amdgcn_exp2f(PRE ? s[nt][t][r + 1] : fmaf(s[nt][t][r + 1], c, -mc));
-                const uint32_t w = pack_bf16x2(x0, x1);
-                pk[nt][t][r >> 1] = w;
-                ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
-                                                                   ones, ls[(r >> 1) & 3], false);
+                pk[nt][t][r >> 1] = pack_bf16x2(x0, x1);
+                ls[(r >> 1) & 3] += x0;
+                ls[(r >> 1) & 3] += x1;
             }
         lsum[nt] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
