@@ -531,6 +531,67 @@ __device__ inline void pv_tile(const u16* Vs, const TileP& pk, RowState<D>& st, 
     }
 }
 
+// pv_tile for the previous key tile, then qk_tile for this one, as one
+// software pipeline: every MFMA is followed by the fragment reads of the
+// MFMA AHEAD places later, across the boundary between the two products, so
+// the scores do not start with an LDS round trip.  Copies of cp spread
+// through the PV MFMAs, those of cq through the score MFMAs.
+template <int D, class CP, class CQ, bool PRE>
+__device__ inline void pv_qk_tile(const u16* Vs, const u16* Ks, const bf16x8 (*qf)[D / 16],
+                                  const TileP& pk, TileScores& s, RowState<D>& st, const CP& cp,
+                                  const CQ& cq, const f32x16* init) {
+    static_assert(kNT == 1, "one MFMA per fragment");
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NF = (kBN / 16) * (D / 32);  // PV fragments, 2 reads each
+    constexpr int NK = 2 * (D / 16);           // K fragments, 1 read each
+    constexpr int AHEAD = 2;  // measured better than 3 or 4 at D=128
+#pragma unroll
+    for (int c4 = 0; c4 < kBN / 16; ++c4) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const bf16x8 vf = v_frag<D>(Vs, dt, c4, lane);
+            const uint32_t* w = &pk[0][c4 >> 1][4 * (c4 & 1)];
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            st.o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.o[0][dt], 0, 0, 0);
+            const int f = c4 * (D / 32) + dt;
+#pragma unroll
+            for (int j = 0; j < CP::N; ++j)
+                if (copy_slot(j, CP::N, NF) == f) cp.issue(j);
+        }
+    }
+    s[0][0] = s[0][1] = PRE ? init[0] : f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a0 = k_frag<D>(Ks, 0, kk, lane), a1 = k_frag<D>(Ks, 1, kk, lane);
+        s[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0][kk], s[0][0], 0, 0, 0);
+        s[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0][kk], s[0][1], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < CQ::N; ++j) {
+            const int sl = copy_slot(j, CQ::N, NK);
+            if (sl >= 2 * kk && sl < 2 * (kk + 1)) cq.issue(j);
+        }
+    }
+    // MFMA i (PV for i < NF, scores after) is followed by the reads of MFMA
+    // i + AHEAD: two transposing reads for a V fragment, one for a K fragment
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NF + NK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        const int g = i + AHEAD;
+        if (g < NF)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (g < NF + NK)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int j = 0; j < CP::N; ++j)
+            if (i < NF && copy_slot(j, CP::N, NF) == i) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+#pragma unroll
+        for (int j = 0; j < CQ::N; ++j)
+            if (i >= NF && copy_slot(j, CQ::N, NK) == i - NF)
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+}
+
 template <int D>
 __device__ inline void rescale(const float* alpha, RowState<D>& st) {
 #pragma unroll
@@ -635,11 +696,15 @@ template <int D, bool QK, bool PV, bool PRE, class CK, class CV>
 __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[D / 16],
                                TileScores& S, const TileP& pk, RowState<D>& st, const CK& ck,
                                const CV& cv) {
-    if (PV) pv_tile<D>(Vs, pk, st, ck);
-    // separate scheduling regions: keeps the fragment prefetch of the two
-    // products from piling up in registers
-    if (PV && QK) __builtin_amdgcn_sched_barrier(0);
-    if (QK) qk_tile<D, CV, NoCopy, PRE>(Ks, qf, S, cv, NoCopy{}, st.mneg);
+    if (PV && QK && D >= 128 && PRE) {
+        pv_qk_tile<D, CK, CV, PRE>(Vs, Ks, qf, pk, S, st, ck, cv, st.mneg);
+    } else {
+        // D=64, and varlen's short items, measured faster with the two
+        // products as separate scheduling regions
+        if (PV) pv_tile<D>(Vs, pk, st, ck);
+        if (PV && QK) __builtin_amdgcn_sched_barrier(0);
+        if (QK) qk_tile<D, CV, NoCopy, PRE>(Ks, qf, S, cv, NoCopy{}, st.mneg);
+    }
     pin_m_outputs<D>(S, st, QK, PV);
 }
 
