@@ -64,6 +64,24 @@ def test_forced_splits_match_oracle(D, splits, monkeypatch):
     compare(out, ref, "splits %d D %d" % (splits, D))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Lkv", [1, 64, 65, 128, 191, 192, 250, 320, 449])
+def test_key_tile_counts(D, Lkv, monkeypatch):
+    """One split over 1..8 key tiles, ragged and exact: the key loop runs in
+    steps of three tiles with one- and two-tile tails, and the last PV product
+    reads the stage of the last tile."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", "1")
+    B, Hq, Hkv, Lq = 1, 8, 2, 32
+    say("key tiles", D, Lkv)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=27)
+    q_pos0 = Lkv - Lq
+    out = _run(q, k, v, q_pos0=q_pos0)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D), q_pos0=q_pos0)
+    compare(out, ref, "D %d Lkv %d" % (D, Lkv))
+    if q_pos0 < 0:
+        assert torch.count_nonzero(out[:, :, :-q_pos0]) == 0
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
 def test_scale_sign_and_zero(scale):
     say("scale", scale)
