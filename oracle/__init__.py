@@ -26,6 +26,7 @@ SEGF_COL = 2
 SEGF_KVEND = 4
 SEGF_ATTR = 8
 SEGF_OVERLAP = 16
+SEGF_SPAN = 32
 
 # Bit meanings of the slot-write token flags.
 KVF_COL = 1

@@ -35,6 +35,8 @@
  *    (kv_end already counts the step's own tokens).
  *  - Varlen with a window on a non-causal segment: only the lower bound
  *    k > p - W applies.
+ *  - Varlen on ring storage: a segment whose visible keys start before
+ *    kv_end - R (positions the ring has overwritten) is flagged and skipped.
  *
  * Numbers: bf16 inputs are widened exactly to double; every product, sum and
  * exponential is double precision (libm exp).  Results are double.
@@ -60,6 +62,8 @@
 #define SEGF_KVEND 4    /* kv_end < 0, or kv_end > rows on flat storage     */
 #define SEGF_ATTR 8     /* seg_attr ring_rows > rows                         */
 #define SEGF_OVERLAP 16 /* a packed row is claimed by two valid segments     */
+#define SEGF_SPAN 32    /* ring storage: the visible keys reach back past the
+                           R positions the ring still holds                   */
 
 static double widen_bf16(uint16_t h)
 {
@@ -232,13 +236,24 @@ int oracle_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 /*
  * Segment checks shared by the varlen oracle's passes.  R is the key-position
  * modulus of the segment (its ring rows, or all rows for flat storage).
+ *
+ * A ring of R rows, written in position order up to kv_end, still holds
+ * positions kv_end - R .. kv_end - 1 only: every older position's row has
+ * been overwritten by a newer one (the batched sequence cache sizes a ring
+ * layer as window + max_write - 1 rows for exactly this reason).  The
+ * earliest key any query of the segment sees is that of its first query,
+ * max(0, kv_end - q_len - W + 1) with a window, 0 without; a ring segment
+ * whose visible keys start before kv_end - R would read overwritten rows,
+ * so it is flagged (SEGF_SPAN) and not attended.
  */
 static int segment_flags(const int32_t *si, const int32_t *attr, int T, int rows,
-                         int cols, int ring_rows_default, int *R_out)
+                         int cols, int ring_rows_default, int window_default,
+                         int *R_out)
 {
     int flags = 0;
     int q_start = si[0], q_len = si[1], col = si[2], kv_end = si[3];
     int ring_rows = attr ? attr[2] : ring_rows_default;
+    int W = attr ? attr[1] : window_default;
     if (q_start < 0 || q_len < 0 || (int64_t)q_start + q_len > T)
         flags |= SEGF_QRANGE;
     if (col < 0 || col >= cols - 1)
@@ -249,6 +264,13 @@ static int segment_flags(const int32_t *si, const int32_t *attr, int T, int rows
     int R = ring ? ring_rows : rows;
     if (kv_end < 0 || (!ring && kv_end > rows))
         flags |= SEGF_KVEND;
+    if (ring && q_len > 0 && kv_end > 0) {
+        int64_t first = W > 0 ? (int64_t)kv_end - q_len - W + 1 : 0;
+        if (first < 0)
+            first = 0;
+        if ((int64_t)kv_end - first > R)
+            flags |= SEGF_SPAN;
+    }
     *R_out = R;
     return flags;
 }
@@ -300,7 +322,7 @@ int oracle_varlen(const uint16_t *q, const uint16_t *ks, const uint16_t *vs,
     for (int s = 0; s < S; s++) {
         int R;
         int f = segment_flags(seq_info + 4 * s, seg_attr ? seg_attr + 3 * s : NULL,
-                              T, rows, cols, ring_rows, &R);
+                              T, rows, cols, ring_rows, window, &R);
         err |= f;
         seg_ok[s] = (f == 0);
         if (!seg_ok[s])
@@ -353,7 +375,7 @@ int oracle_varlen(const uint16_t *q, const uint16_t *ks, const uint16_t *vs,
             int W = seg_attr ? seg_attr[3 * s + 1] : window;
             int R;
             segment_flags(si, seg_attr ? seg_attr + 3 * s : NULL, T, rows, cols,
-                          ring_rows, &R);
+                          ring_rows, window, &R);
             int j = t - q_start;
             int64_t p = (int64_t)kv_end - q_len + j;
             int hk = h / g;

@@ -44,20 +44,41 @@ def prefill(q, k, v, scale, q_pos0, window=0):
     return out
 
 
-def varlen(q, ks, vs, seq_info, seg_attr, scale):
+def ring_holds(R, kv_end):
+    """Which positions a ring of R rows still holds after positions
+    0 .. kv_end - 1 were written in order to rows position mod R: the set of
+    positions x whose row was not overwritten by a later position."""
+    last = {}
+    for pos in range(kv_end):
+        last[pos % R] = pos
+    return {x for r, x in last.items()}
+
+
+def varlen(q, ks, vs, seq_info, seg_attr, scale, stale=None):
     """q [T][Hq][D]; ks/vs [rows][cols][Hkv][D]; seq_info list of 4-tuples;
     seg_attr list of (causal, window, ring_rows) with ring_rows <= 0 meaning
-    all rows.  All segments are assumed valid and disjoint."""
+    all rows.  All segments are assumed in range and disjoint.  A segment
+    that would read a key its ring no longer holds (simulated by ring_holds)
+    is not attended: its rows stay 0 and, when ``stale`` is a list, its
+    index is appended to it."""
     T, Hq, D = len(q), len(q[0]), len(q[0][0])
     rows, Hkv = len(ks), len(ks[0][0])
     g = Hq // Hkv
     out = [[[0.0] * D for _ in range(Hq)] for _ in range(T)]
-    for (q_start, q_len, col, kv_end), (causal, window, ring_rows) in zip(seq_info, seg_attr):
+    for n, ((q_start, q_len, col, kv_end), (causal, window, ring_rows)) in \
+            enumerate(zip(seq_info, seg_attr)):
         R = ring_rows if ring_rows > 0 else rows
+        held = ring_holds(R, kv_end)
+        vis_rows = []
         for j in range(q_len):
             p = kv_end - q_len + j
-            vis = {x for x in range(kv_end)
-                   if (not causal or x <= p) and (window <= 0 or x > p - window)}
+            vis_rows.append({x for x in range(kv_end)
+                             if (not causal or x <= p) and (window <= 0 or x > p - window)})
+        if any(not vis <= held for vis in vis_rows):
+            if stale is not None:
+                stale.append(n)
+            continue
+        for j, vis in enumerate(vis_rows):
             for h in range(Hq):
                 hk = h // g
                 out[q_start + j][h] = _attend(

@@ -70,6 +70,23 @@ def test_golden_ring_varlen_rational():
     torch.testing.assert_close(out, exp, rtol=1e-13, atol=1e-13)
 
 
+def test_golden_noncausal_window_rational():
+    g = json.load(open(os.path.join(GOLDEN, "noncausal_window_rational.json")))
+    rows, cols = g["rows"], g["cols"]
+    nan = float("nan")
+    ks = torch.full((rows, cols, 1, 2), nan)
+    vs = torch.full((rows, cols, 1, 2), nan)
+    ks[:, 0, 0, :] = torch.tensor([[float(x) for x in r] for r in g["k_col0"]])
+    vs[:, 0, 0, :] = torch.tensor([[float(x) for x in r] for r in g["v_col0"]])
+    out, flags = oracle.varlen(_bf(g["q"]), ks.to(torch.bfloat16), vs.to(torch.bfloat16),
+                               g["seq_info"], seg_attr=g["seg_attr"], scale=_scale(g["scale"]),
+                               return_flags=True)
+    assert flags == 0
+    exp = torch.tensor([[[float(Fraction(x)) for x in h] for h in t] for t in g["out"]],
+                       dtype=torch.float64)
+    torch.testing.assert_close(out, exp, rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------------------------------- brute force
 
 @pytest.mark.parametrize("Lq,Lkv,q_pos0,window", [
@@ -357,10 +374,47 @@ def test_ring_of_window_plus_max_write_minus_one_rows_holds_every_visible_key():
     a = oracle.varlen(q, ring_k, ring_v, seg, seg_attr=[(1, W, R)], scale=0.3)
     b = oracle.varlen(q, flat_k, flat_v, seg, seg_attr=[(1, W, 0)], scale=0.3)
     assert torch.equal(a, b)
-    # one more key per window (W + 1) on the same ring no longer matches flat
-    a1 = oracle.varlen(q, ring_k, ring_v, seg, seg_attr=[(1, W + 1, R)], scale=0.3)
+    # one more key per window (W + 1): the first query would reach a position
+    # the ring has overwritten, so the segment is flagged and not attended
+    a1, f1 = oracle.varlen(q, ring_k, ring_v, seg, seg_attr=[(1, W + 1, R)], scale=0.3,
+                           return_flags=True)
     b1 = oracle.varlen(q, flat_k, flat_v, seg, seg_attr=[(1, W + 1, 0)], scale=0.3)
-    assert not torch.equal(a1, b1)
+    assert f1 == oracle.SEGF_SPAN and torch.count_nonzero(a1) == 0
+    assert torch.count_nonzero(b1) > 0
+
+
+@pytest.mark.parametrize("causal,W,q_len,kv_end,R,stale", [
+    (1, 6, 4, 23, 9, False),    # W + q_len - 1 = R: every visible key is held
+    (1, 7, 4, 23, 9, True),     # one key more than the ring holds
+    (1, 0, 1, 9, 9, False),     # no window, ring not yet wrapped
+    (1, 0, 1, 10, 9, True),     # no window, wrapped: key 0 was overwritten
+    (0, 6, 4, 23, 9, False),    # non-causal: the window is the lower bound only
+    (0, 7, 4, 23, 9, True),
+    (1, 6, 4, 7, 9, False),     # fewer keys than rows
+    (1, 3, 0, 50, 9, False),    # no queries: nothing is read
+    (1, 30, 2, 2, 9, False),    # window past position 0
+])
+def test_ring_span_flag_matches_the_simulated_ring(causal, W, q_len, kv_end, R, stale):
+    """A ring segment is attended only when every key its queries see is still
+    held by the ring (positions written in order, later ones overwriting the
+    row of earlier ones); otherwise it is flagged SEGF_SPAN and its rows are 0.
+    Expected answers come from the written-in-order simulation in brute.py and
+    are checked against the hand-derived column above."""
+    rows, cols, Hkv, D, Hq = 12, 2, 1, 4, 1
+    ks, vs = _store(rows, cols, Hkv, D, 101)
+    q = synth.randn_bf16((max(q_len, 1), Hq, D), 103)
+    info, attr = [(0, q_len, 0, kv_end)], [(causal, W, R)]
+    got, f = oracle.varlen(q, ks, vs, info, seg_attr=attr, scale=0.5, return_flags=True)
+    found = []
+    ref = brute.varlen(_lists(q), _lists(ks), _lists(vs), info, attr, 0.5, stale=found)
+    assert bool(found) == stale
+    assert f == (oracle.SEGF_SPAN if stale else 0)
+    torch.testing.assert_close(got, torch.tensor(ref, dtype=torch.float64), rtol=1e-12,
+                               atol=1e-12)
+    # flat storage of the same rows never sets the flag
+    _, f2 = oracle.varlen(q, ks, vs, [(0, q_len, 0, min(kv_end, rows))],
+                          seg_attr=[(causal, W, 0)], scale=0.5, return_flags=True)
+    assert f2 == 0
 
 
 def test_varlen_segment_order_and_foreign_columns_do_not_matter():
@@ -512,11 +566,13 @@ def test_kv_write_then_attend_reads_the_written_key():
     for t in range(2):
         for h in range(Hq):
             assert torch.equal(out[t, h], vn[t, h // g].double())
-    # a plain causal segment sees the new key at its own position as well
-    full = oracle.varlen(q[:1], k2, v2, info[:1], seg_attr=torch.tensor([(1, 0, R)],
+    # a causal segment with the widest window its ring holds (R keys) sees
+    # the new key at its own position as well
+    full = oracle.varlen(q[:1], k2, v2, info[:1], seg_attr=torch.tensor([(1, R, R)],
                                                                      dtype=torch.int32))
-    stale = oracle.varlen(q[:1], ks, vs, info[:1], seg_attr=torch.tensor([(1, 0, R)],
+    stale = oracle.varlen(q[:1], ks, vs, info[:1], seg_attr=torch.tensor([(1, R, R)],
                                                                       dtype=torch.int32))
+    assert torch.count_nonzero(full) > 0
     assert not torch.allclose(full, stale)
 
 
@@ -551,7 +607,9 @@ def test_prefill_vs_brute_random(Hkv, g, Lq, Lkv, q_pos0, window, D, seed):
 def test_varlen_vs_brute_random(data):
     """Random tiny tables of disjoint segments over a small store: causal or
     not, windows, ring moduli (wrapped or not), queries before the first key;
-    the oracle equals the brute force to 1e-12 and uncovered rows are zero."""
+    the oracle equals the brute force to 1e-12, uncovered rows are zero, and
+    exactly the segments that would read a position their ring no longer
+    holds are flagged."""
     rows = data.draw(hst.integers(2, 10))
     cols = data.draw(hst.integers(2, 4))
     Hkv = data.draw(hst.integers(1, 2))
@@ -579,7 +637,8 @@ def test_varlen_vs_brute_random(data):
     scale = 0.5
     got, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr or None, scale=scale,
                                return_flags=True)
-    assert flags == 0
-    ref = brute.varlen(_lists(q), _lists(ks), _lists(vs), info, attr, scale)
+    stale = []
+    ref = brute.varlen(_lists(q), _lists(ks), _lists(vs), info, attr, scale, stale=stale)
+    assert flags == (oracle.SEGF_SPAN if stale else 0)
     torch.testing.assert_close(got, torch.tensor(ref, dtype=torch.float64).reshape(T, Hq, D),
                                rtol=1e-12, atol=1e-12)
