@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
-SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP = 1, 2, 4, 8, 16
+SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP, SEG_SPAN = 1, 2, 4, 8, 16, 32
 KV_COL, KV_POS, KV_ROWS = 1, 2, 4
 BOUND_KV, BOUND_QPOS = 1, 2
 
@@ -111,6 +111,22 @@ def _gpu(t, name):
         raise ValueError("%s must be bfloat16" % name)
 
 
+def _same_device(named):
+    """Every given tensor on the device of the first (the kernels take raw
+    pointers, so a tensor elsewhere would be read as device memory)."""
+    named = [(t, n) for t, n in named if t is not None]
+    d0 = named[0][0].device
+    for t, n in named[1:]:
+        if t.device != d0:
+            raise ValueError("%s is on %s, %s on %s: all tensors must be on one device"
+                             % (n, t.device, named[0][1], d0))
+
+
+def _check_out(out, shape):
+    if out is not None and tuple(out.shape) != tuple(shape):
+        raise ValueError("out has shape %s, %s expected" % (tuple(out.shape), tuple(shape)))
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None
@@ -134,18 +150,17 @@ def causal_prefill(q, k, v, out=None, scale=None, q_pos0=None, window=0, workspa
     q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D] bf16 on the device, any strides with a
     unit innermost stride.  Returns ``out`` ([B,Hq,Lq,D] bf16).
     """
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _gpu(t, n)
     B, Hq, Lq, D = q.shape
     Bk, Hkv, Lkv, Dk = k.shape
     if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
         raise ValueError("q/k/v shapes do not agree: %s %s %s" % (q.shape, k.shape, v.shape))
+    _check_out(out, (B, Hq, Lq, D))
+    _same_device([(q, "q"), (k, "k"), (v, "v"), (out, "out"), (workspace, "workspace")])
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is not None:
+            _gpu(t, n)
     if out is None:
         out = torch.empty((B, Hq, Lq, D), dtype=torch.bfloat16, device=q.device)
-    else:
-        _gpu(out, "out")
-        if tuple(out.shape) != (B, Hq, Lq, D):
-            raise ValueError("out has shape %s" % (tuple(out.shape),))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if q_pos0 is None:
@@ -170,19 +185,22 @@ def causal_prefill_dev(q, k, v, bounds, out=None, scale=None, window=0, workspac
     int64 tensor [2] = (q_pos0, kv_len); k/v [B,Hkv,Lkv,D] hold Lkv >= kv_len
     keys of capacity.  Returns (out, workspace); read the bound flags with
     ``prefill_read_error(workspace)``."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _gpu(t, n)
-    if bounds.dtype != torch.int64 or not bounds.is_cuda or not bounds.is_contiguous() or \
-            bounds.numel() != 2:
-        raise ValueError("bounds must be a contiguous int64 device tensor of 2 entries")
     B, Hq, Lq, D = q.shape
     Bk, Hkv, Lkv, Dk = k.shape
     if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
         raise ValueError("q/k/v shapes do not agree: %s %s %s" % (q.shape, k.shape, v.shape))
+    _check_out(out, (B, Hq, Lq, D))
+    if bounds.dtype != torch.int64 or not bounds.is_contiguous() or bounds.numel() != 2:
+        raise ValueError("bounds must be a contiguous int64 device tensor of 2 entries")
+    _same_device([(q, "q"), (k, "k"), (v, "v"), (bounds, "bounds"), (out, "out"),
+                  (workspace, "workspace")])
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is not None:
+            _gpu(t, n)
+    if not bounds.is_cuda:
+        raise ValueError("bounds must be a contiguous int64 device tensor of 2 entries")
     if out is None:
         out = torch.empty((B, Hq, Lq, D), dtype=torch.bfloat16, device=q.device)
-    else:
-        _gpu(out, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     with torch.cuda.device(q.device):
@@ -218,25 +236,29 @@ def sdpa_varlen(q, k_store, v_store, seq_info, seg_attr=None, out=None, scale=No
     least ``varlen_workspace_bytes``) to keep the call allocation-free, e.g.
     under graph capture; read its error word with ``varlen_read_error``.
     """
-    for t, n in ((q, "q"), (k_store, "k_store"), (v_store, "v_store")):
-        _gpu(t, n)
     T, Hq, D = q.shape
     rows, cols, Hkv, Dk = k_store.shape
     if Dk != D or tuple(v_store.shape) != tuple(k_store.shape):
         raise ValueError("store shapes do not agree")
-    if seq_info.dtype != torch.int32 or not seq_info.is_cuda or not seq_info.is_contiguous():
+    _check_out(out, (T, Hq, D))
+    if seq_info.dtype != torch.int32 or not seq_info.is_contiguous():
         raise ValueError("seq_info must be a contiguous int32 device tensor")
     S = seq_info.shape[0] if seq_info.numel() else 0
     if seq_info.numel() and tuple(seq_info.shape) != (S, 4):
         raise ValueError("seq_info must be [S, 4]")
     if seg_attr is not None:
-        if (seg_attr.dtype != torch.int32 or not seg_attr.is_cuda or
-                not seg_attr.is_contiguous() or tuple(seg_attr.shape) != (S, 3)):
+        if (seg_attr.dtype != torch.int32 or not seg_attr.is_contiguous() or
+                tuple(seg_attr.shape) != (S, 3)):
             raise ValueError("seg_attr must be a contiguous int32 device tensor [S, 3]")
+    _same_device([(q, "q"), (k_store, "k_store"), (v_store, "v_store"), (seq_info, "seq_info"),
+                  (seg_attr, "seg_attr"), (out, "out"), (workspace, "workspace")])
+    for t, n in ((q, "q"), (k_store, "k_store"), (v_store, "v_store"), (out, "out")):
+        if t is not None:
+            _gpu(t, n)
+    if not seq_info.is_cuda:
+        raise ValueError("seq_info must be a contiguous int32 device tensor")
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
-    else:
-        _gpu(out, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     with torch.cuda.device(q.device):
@@ -290,6 +312,9 @@ def kv_write(k_new, v_new, k_store, v_store, positions, seq_cols, slot_rows=None
     else rows).  positions int64 [T], seq_cols / slot_rows int32 [T], device
     tensors.  Returns the workspace that holds the error word (read it with
     ``kv_write_read_error``)."""
+    _same_device([(k_store, "k_store"), (v_store, "v_store"), (k_new, "k_new"),
+                  (v_new, "v_new"), (positions, "positions"), (seq_cols, "seq_cols"),
+                  (slot_rows, "slot_rows"), (workspace, "workspace")])
     for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_store, "k_store"), (v_store, "v_store")):
         _gpu(t, n)
     T, Hkv, D = k_new.shape

@@ -1,28 +1,37 @@
 // attn.hip -- causal GQA prefill and varlen SDPA for MI355X (gfx950, CDNA4).
 //
-// Flash-style attention: one pass over the keys with an online softmax
-// (exact running maximum, fp32 running sum, fp32 accumulator), bf16 MFMA for
-// both contractions, K/V tiles staged through LDS and shared by every query
-// head of a GQA group.  The operation is defined in
-// "[CUDA] Use Triton TMA for long-context causal prefill" (Summary) and
-// "[executorch][cuda] Add a length-aware Triton SDPA over per-sequence KV
-// columns" (description); the C ABI is declared in include/attn.h.
+// Flash-style attention: one pass over the keys with a streaming softmax
+// (fp32 row sums, fp32 accumulators), bf16 MFMA for both contractions, K/V
+// tiles staged through LDS and shared by every query head of a GQA group.
+// The operation is defined in "[CUDA] Use Triton TMA for long-context causal
+// prefill" (Summary) and "[executorch][cuda] Add a length-aware Triton SDPA
+// over per-sequence KV columns" (description); the C ABI is declared in
+// include/attn.h.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows):
+// Softmax: the first key tile of a range fixes each row's reference (its
+// exact maximum over that tile) and later tiles take exponentials against
+// it, with no per-tile maxima and no rescales.  Softmax does not depend on
+// the reference, so this is exact while nothing overflows or underflows;
+// every row checks its sum afterwards, and a workgroup with a row outside
+// [2^-64, 2^64] redoes its range with the exact running maximum.
+//
+// Work decomposition (D = 64, 128: one workgroup = 8 waves = 256 query rows):
 //   rows of a workgroup = (query heads of one KV head) x (query positions);
-//   each wave owns 32 rows and keeps Q, the output accumulator, the running
-//   maximum and the running sum in registers for the whole key range.
-//   Keys stream in tiles of 64: K as [key][d] and V transposed as [d][key]
-//   in LDS; the next tile's global loads are in flight while the current
-//   tile is computed.
+//   each wave owns 32 rows and keeps Q, the output accumulator, the row
+//   reference and the running sum in registers for the whole key range.
+//   Waves 0-3 and 4-7 form two groups that alternate MFMA and softmax phases
+//   one phase apart (one wave of each group per SIMD).  Keys stream in tiles
+//   of 64 through three LDS stages each of K and V, both in their natural
+//   [key][d] order with XOR-swizzled 16-byte chunks.  D = 256 has its own
+//   kernel of 4 waves (one per SIMD) over two stages.
 //
 // MFMA layout (v_mfma_f32_32x32x16_bf16): the score tile is computed
 // transposed, S^T = K Q^T (keys x rows), so each lane holds 16 scores of ONE
-// query row: row maxima and sums are in-lane plus a single exchange between
-// lanes l and l+32.  The same registers, rounded to bf16, are directly the
-// B operand of O^T = V^T P^T; V^T is stored in LDS with the key order inside
-// each 16-key group permuted (bits 2 and 3 of the key index swapped) to
-// match which keys each lane holds.
+// query row: row sums are in-lane plus a single exchange between lanes l and
+// l+32.  The same registers, rounded to bf16, are directly the B operand of
+// O^T = V^T P^T; the V^T operand comes from the [key][d] tile through the
+// transposing LDS read (ds_read_b64_tr_b16), with the key order inside each
+// 16-key group matched to which keys each lane holds.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -1464,6 +1473,13 @@ __device__ inline Segment read_segment(const VarlenArgs& a, int s) {
     bool ring = ring_rows > 0;
     g.R = ring ? ring_rows : a.rows;
     if (g.kv_end < 0 || (!ring && g.kv_end > a.rows)) f |= ATTN_SEG_KVEND;
+    // a ring of R rows holds positions kv_end - R .. kv_end - 1 only; the
+    // earliest key any query of the segment sees is its first query's
+    if (ring && g.q_len > 0 && g.kv_end > 0) {
+        int64_t first = g.window > 0 ? (int64_t)g.kv_end - g.q_len - g.window + 1 : 0;
+        if (first < 0) first = 0;
+        if ((int64_t)g.kv_end - first > g.R) f |= ATTN_SEG_SPAN;
+    }
     g.flags = f;
     return g;
 }
@@ -2176,7 +2192,7 @@ size_t attn_causal_prefill_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, in
 
 // Both prefill entry points: with bounds (device (q_pos0, kv_len)), the
 // workspace starts with the 256-byte error word and the partials follow.
-int prefill_call(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+static int prefill_call(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
                  int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
                  const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
                  int64_t q_pos0, const int64_t* bounds, int window, void* workspace,
@@ -2483,7 +2499,7 @@ int attn_varlen_read_error(const void* workspace, int S, int T, void* stream, in
     return ATTN_OK;
 }
 
-int kv_write_blocks(int T) { return T > 0 ? (T + kWriteTokens - 1) / kWriteTokens : 0; }
+static int kv_write_blocks(int T) { return T > 0 ? (T + kWriteTokens - 1) / kWriteTokens : 0; }
 
 size_t attn_kv_write_workspace(int T) {
     if (T < 0) return 0;

@@ -41,7 +41,11 @@ typedef enum {
 #define ATTN_SEG_KVEND 4    /* kv_end < 0, or kv_end > rows on flat storage        */
 #define ATTN_SEG_ATTR 8     /* seg_attr ring_rows > rows                           */
 #define ATTN_SEG_OVERLAP 16 /* a packed row claimed by two valid segments; the
-                               outputs of those rows are then unspecified          */
+                               whole output of the call is then unspecified        */
+#define ATTN_SEG_SPAN 32    /* ring storage: a query would see a key older than
+                               kv_end - R, whose ring row a later position has
+                               overwritten (the window is wider than
+                               R - q_len + 1, or absent with kv_end > R)          */
 
 /* Bits of the slot-write error word (attn_kv_write_read_error).  A flagged
  * token is not written. */
@@ -78,7 +82,10 @@ const char *attn_last_error(void);
  * sees key j iff 0 <= j < Lkv, j <= q_pos0 + i and, when window > 0,
  * j > q_pos0 + i - window (window keys including its own position).
  * o = sum_j softmax_j(scale * q.k_j) v_j over the visible keys; a row with
- * no visible key is written as exact zeros.
+ * no visible key is written as exact zeros.  Keys past a workgroup's range
+ * are never loaded; a NaN in a V row inside it that some of its rows do not
+ * see still reaches those rows (0 * NaN), see the limitation under
+ * attn_sdpa_varlen.
  *
  * Layout rules (else ATTN_ERR_UNSUPPORTED): D in {64, 128, 256} (256: the
  * head dimension the page left on its portable path, here a kernel of its
@@ -138,15 +145,17 @@ int attn_prefill_read_error(const void *workspace, void *stream, int32_t *err_ou
  * Length-aware varlen SDPA over per-sequence KV columns.
  *
  * Defines ("[executorch][cuda] Add a length-aware Triton SDPA over
- * per-sequence KV columns", description and the stacked commits on the
- * batched-sequence manifest layout and the batched sequence cache): each
- * resident sequence owns one column of a [rows, cols, Hkv, D] store whose
- * last column is scratch; the device table seq_info Int32[S,4] =
- * (q_start, q_len, col, kv_end) says which packed query rows belong to which
- * column and how many keys that sequence holds (the step's own tokens
- * included).  Query j of a segment sits at position kv_end - q_len + j.  A
- * key at position k is stored at row (k mod R) of its column, where R is the
- * segment's ring rows (ring storage) or rows (flat storage).
+ * per-sequence KV columns", description; the stacked commits on the
+ * batched-sequence manifest layout and the batched sequence cache give the
+ * store layout, the slot rule and the ring size).  The K/V store is a grid
+ * of rows x cols slots per KV head; a sequence keeps its keys in one column,
+ * and the last column is reserved for padding writes, so it is never read.
+ * A segment s of the table is one run of packed query rows
+ * [q_start, q_start + q_len) that attends column col, where kv_end is the
+ * sequence's key count after this step's own tokens were written.  Its
+ * query j therefore has position kv_end - q_len + j, and key position k is
+ * found in row k mod R of the column (R = the segment's ring rows on ring
+ * storage, else rows).
  *
  *   q        [T, Hq, D]           bf16 packed query rows, strides q_str[3]
  *   k_store,
@@ -157,22 +166,33 @@ int attn_prefill_read_error(const void *workspace, void *stream, int32_t *err_ou
  *            (causal, window, ring_rows); when NULL every segment takes the
  *            call's causal / window / ring_rows.
  *
- * Visibility of key k for a query at position p: k < kv_end, k <= p when
- * causal, k > p - window when window > 0.  ring_rows <= 0 means flat
- * storage.  Packed rows in [0, T) that no valid segment covers are written
- * as zeros, in the same call.  The host never reads seq_info / seg_attr:
- * launch geometry depends only on (S, T, Hq, Hkv, D, rows, cols), so one
- * captured graph serves any lengths written into the same buffers.
- * Invalid segments are skipped, zeroed and reported in the error word.
+ * A query at position p sees key k iff k < kv_end, k <= p when causal, and
+ * k > p - window when window > 0 (on a non-causal segment the window is this
+ * lower bound only).  ring_rows <= 0 means flat storage.  Packed rows of
+ * [0, T) that belong to no valid segment come back as zeros from the same
+ * call.  The host never reads seq_info / seg_attr: the launch geometry is a
+ * function of (S, T, Hq, Hkv, D, rows, cols) only, so one captured graph
+ * serves every table later written into the same buffers.  A segment that
+ * breaks a rule is not attended: its rows are zeroed and its ATTN_SEG_* bit
+ * is set in the error word.
  *
- * Layout rules as for prefill (else ATTN_ERR_UNSUPPORTED).  Sizes (else
- * ATTN_ERR_INVALID): non-null stores, q/out non-null when T > 0,
+ * Limitation (NaN): keys outside every workgroup's key range are never
+ * loaded, so NaN or Inf there (later positions, other columns, the scratch
+ * column, overwritten ring rows) cannot reach the output.  A V row inside a
+ * workgroup's key range that is masked for some of its rows enters their PV
+ * product with weight 0, and 0 * NaN = NaN: a NaN in such a V row spreads to
+ * the rows of that workgroup.  The same holds for attn_causal_prefill.
+ *
+ * Layout rules as for prefill (else ATTN_ERR_UNSUPPORTED); D in {64, 128}.
+ * Sizes (else ATTN_ERR_INVALID): non-null stores, q/out non-null when T > 0,
  * S >= 0, T >= 0, rows >= 1, cols >= 2,
  * S <= 2 * (cols - 1), Hq % Hkv == 0, ring_rows <= rows, and no window on a
  * non-causal call when seg_attr is NULL.
  *
  * workspace: at least attn_sdpa_varlen_workspace(...) bytes, 256-byte
- * aligned; it holds the error word and split partials.
+ * aligned; it holds the error words and split partials.  Its size query
+ * takes cols too (beyond the sizes of the call that determine the layout),
+ * so that one signature validates every argument the call checks.
  */
 size_t attn_sdpa_varlen_workspace(int S, int T, int Hq, int Hkv, int D, int rows, int cols);
 
@@ -188,7 +208,9 @@ int attn_sdpa_varlen(const void *q, const void *k_store, const void *v_store, vo
  * Reads the error word of the last attn_sdpa_varlen call that used this
  * workspace (an OR of ATTN_SEG_* bits, 0 when every segment was valid).
  * Synchronises `stream` first.  The arguments (S, T) must be those of that
- * call.
+ * call: the flags are kept as several words (each written by one workgroup
+ * with a plain store, so no call needs a clearing pass), and (S, T) say how
+ * many to OR.
  */
 int attn_varlen_read_error(const void *workspace, int S, int T, void *stream,
                            int32_t *err_out);

@@ -48,6 +48,20 @@ def test_library_exports_every_declared_function():
     assert L.attn_abi_version() == 1
 
 
+def test_library_exports_nothing_else():
+    """Only the declared entry points have external linkage."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    _lib()
+    out = subprocess.run([nm, "-D", "--defined-only", attn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+    assert funcs == declared_functions(), funcs
+
+
 def _prefill(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64, scale=0.125,
              qs=None, ks=None, vs=None, os_=None, q_pos0=8, window=0):
     L = _lib()
@@ -186,6 +200,49 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.causal_prefill(q, q[:, :1], q[:, :1])
+
+
+def test_binding_checks_out_shapes_before_any_call():
+    """A too-small out would let a kernel write past it, so every entry point
+    checks it against q (prefill [B,Hq,Lq,D], varlen [T,Hq,D])."""
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    small = torch.zeros(1, 2, 3, 64, dtype=torch.bfloat16)
+    bounds = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="out has shape"):
+        attn.causal_prefill(q, kv, kv, out=small)
+    with pytest.raises(ValueError, match="out has shape"):
+        attn.causal_prefill_dev(q, kv, kv, bounds, out=small)
+    qv = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    store = torch.zeros(16, 3, 2, 64, dtype=torch.bfloat16)
+    info = torch.zeros(1, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="out has shape"):
+        attn.sdpa_varlen(qv, store, store, info, out=torch.zeros(9, 4, 64, dtype=torch.bfloat16))
+
+
+def test_binding_checks_that_every_tensor_is_on_one_device():
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    meta = torch.empty(1, 1, 8, 64, dtype=torch.bfloat16, device="meta")
+    with pytest.raises(ValueError, match="one device"):
+        attn.causal_prefill(q, kv, meta)
+    with pytest.raises(ValueError, match="one device"):
+        attn.causal_prefill_dev(q, kv, kv, torch.zeros(2, dtype=torch.int64, device="meta"))
+    qv = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    store = torch.zeros(16, 3, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="one device"):
+        attn.sdpa_varlen(qv, store, store, torch.zeros(1, 4, dtype=torch.int32, device="meta"))
+    with pytest.raises(ValueError, match="one device"):
+        attn.kv_write(torch.zeros(2, 2, 64, dtype=torch.bfloat16),
+                      torch.zeros(2, 2, 64, dtype=torch.bfloat16), store, store,
+                      torch.zeros(2, dtype=torch.int64, device="meta"),
+                      torch.zeros(2, dtype=torch.int32))
+
+
+def test_span_flag_bits_match_the_oracle():
+    assert (attn.SEG_QRANGE, attn.SEG_COL, attn.SEG_KVEND, attn.SEG_ATTR, attn.SEG_OVERLAP,
+            attn.SEG_SPAN) == (oracle.SEGF_QRANGE, oracle.SEGF_COL, oracle.SEGF_KVEND,
+                               oracle.SEGF_ATTR, oracle.SEGF_OVERLAP, oracle.SEGF_SPAN)
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

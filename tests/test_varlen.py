@@ -38,7 +38,7 @@ def test_pinned_table_matches_oracle():
     assert torch.count_nonzero(out[(~covered).to(dev())]) == 0
 
 
-@pytest.mark.parametrize("seed", [5001, 5002, 5003, 5004])
+@pytest.mark.parametrize("seed", range(5001, 5011))
 def test_seeded_tables_match_oracle(seed):
     say("varlen seeded table", seed)
     st = synth.VARLEN_STORE
@@ -250,15 +250,43 @@ def test_call_level_modes_without_seg_attr():
 def test_small_rings_wrap_inside_a_tile(D):
     """Ring storage of fewer rows than a 64-key tile (5, 37, 63) and around it
     (64, 65): one tile's keys wrap the ring several times; compute-path and
-    decode-path segments, each window no longer than its ring."""
+    decode-path segments, each with the widest window its ring holds
+    (R - q_len + 1 keys)."""
     say("varlen small rings D=%d" % D)
     rows, cols, Hkv, Hq = 200, 6, 2, 8
     info = torch.tensor([(0, 20, 0, 300), (24, 3, 1, 500), (30, 10, 2, 129),
                          (45, 8, 3, 1000), (60, 2, 4, 777)], dtype=torch.int32)
-    attr = torch.tensor([(1, 37, 37), (1, 5, 5), (1, 63, 63), (1, 64, 64), (1, 65, 65)],
+    attr = torch.tensor([(1, 18, 37), (1, 3, 5), (1, 54, 63), (1, 57, 64), (1, 64, 65)],
                         dtype=torch.int32)
     q, ks, vs = synth.varlen_inputs(70, rows, cols, Hkv, D, Hq, wid=46)
     out, err = _gpu_varlen(q, ks, vs, info, attr)
     ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
     assert err == flags == 0
     compare(out, ref, "small rings")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_ring_segments_past_their_span_are_flagged(D):
+    """Ring segments whose queries would see a position the ring has
+    overwritten (no window with kv_end > R; a window wider than R - q_len + 1;
+    the same on a non-causal segment) are flagged ATTN_SEG_SPAN and zeroed,
+    next to valid ring and flat segments that are attended."""
+    say("varlen ring span flag D", D)
+    rows, cols, Hkv, Hq = 3000, 8, 2, 16
+    info = torch.tensor([(0, 16, 0, 5000),   # ring 2559, no window: stale
+                         (20, 512, 1, 8000), # window 2049 + 512 - 1 > 2559: stale
+                         (540, 4, 2, 6000),  # non-causal, window 2557: stale
+                         (550, 512, 3, 8000),  # window 2048: exactly the ring
+                         (1070, 16, 4, 2500),  # ring not yet wrapped, no window
+                         (1090, 33, 5, 2900)],  # flat
+                        dtype=torch.int32)
+    attr = torch.tensor([(1, 0, 2559), (1, 2049, 2559), (0, 2557, 2559), (1, 2048, 2559),
+                         (1, 0, 2559), (1, 0, 0)], dtype=torch.int32)
+    T = 1130
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=51)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == attn.SEG_SPAN
+    compare(out, ref, "ring span D%d" % D)
+    assert torch.count_nonzero(out[:544]) == 0
+    assert torch.count_nonzero(out[550:1062]) > 0
