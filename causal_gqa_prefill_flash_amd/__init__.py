@@ -49,6 +49,9 @@ def lib():
     L.attn_causal_prefill.restype = I
     L.attn_causal_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float,
                                       I64A, I64A, I64A, I64A, I64, I, P, SZ, P]
+    L.attn_causal_prefill_noalloc.restype = I
+    L.attn_causal_prefill_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_float,
+                                              I64A, I64A, I64A, I64A, I64, I, P]
     L.attn_causal_prefill_dev_workspace.restype = SZ
     L.attn_causal_prefill_dev_workspace.argtypes = [I, I, I, I, I, I]
     L.attn_causal_prefill_dev.restype = I
@@ -172,6 +175,36 @@ def causal_prefill(q, k, v, out=None, scale=None, q_pos0=None, window=0, workspa
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lkv, D, float(scale),
             _strides(q, 4), _strides(k, 4), _strides(v, 4), _strides(out, 4),
             int(q_pos0), int(window), _ptr(ws), need, _stream())
+    _check(st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def causal_prefill_noalloc(q, k, v, out, scale=None, q_pos0=None, window=0):
+    """causal_prefill through the entry point that allocates nothing: the
+    split partials live in the library's static device buffer
+    (NOALLOC_SCRATCH_BYTES per device, shared by every such call on that
+    device, so calls that overlap in time race).  ``out`` must be given, so
+    that this call allocates nothing either."""
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q/k/v shapes do not agree: %s %s %s" % (q.shape, k.shape, v.shape))
+    _check_out(out, (B, Hq, Lq, D))
+    _same_device([(q, "q"), (k, "k"), (v, "v"), (out, "out")])
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _gpu(t, n)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q_pos0 is None:
+        q_pos0 = Lkv - Lq
+    with torch.cuda.device(q.device):
+        st = lib().attn_causal_prefill_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lkv, D, float(scale),
+            _strides(q, 4), _strides(k, 4), _strides(v, 4), _strides(out, 4),
+            int(q_pos0), int(window), _stream())
     _check(st)
     return out
 

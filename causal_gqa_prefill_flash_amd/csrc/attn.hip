@@ -49,6 +49,12 @@
 
 #include "attn.h"
 
+// Split partials of attn_causal_prefill_noalloc: a library-owned buffer for
+// callers that cannot allocate.  Host code never uses this name as an
+// address (in host code it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 typedef uint16_t u16;
@@ -2173,6 +2179,28 @@ size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
     return bytes;
 }
 
+// Device address of `scratch` on each device, taken once per device with
+// that device current (each device holds its own copy of the array).
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_HIP, "hipGetDevice failed");
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            p = nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    });
+    if (!g_scratch_ptr[dev]) return fail(ATTN_ERR_HIP, "could not read the scratch buffer's address");
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2196,7 +2224,7 @@ static int prefill_call(const void* q, const void* k, const void* v, void* out, 
                  int Lq, int Lkv, int D, float scale, const int64_t q_str[4],
                  const int64_t k_str[4], const int64_t v_str[4], const int64_t o_str[4],
                  int64_t q_pos0, const int64_t* bounds, int window, void* workspace,
-                 size_t ws_bytes, void* stream) {
+                 size_t ws_bytes, void* stream, bool use_scratch = false) {
     clear_err();
     if (!q_str || !k_str || !v_str || !o_str) return fail(ATTN_ERR_INVALID, "null stride array");
     if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 0 || Lkv < 0)
@@ -2231,6 +2259,16 @@ static int prefill_call(const void* q, const void* k, const void* v, void* out, 
     const int nsplit = prefill_splits(B, Hq, Hkv, Lq, Lkv, D, di);
     const size_t errb = bounds ? 256 : 0;
     const size_t need = errb + prefill_ws_bytes(B, Hq, Lq, D, nsplit);
+    if (use_scratch && need > 0) {
+        // the partials go to the static buffer instead of a caller workspace
+        if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+            return fail(ATTN_ERR_WORKSPACE,
+                        "split partials of %zu bytes exceed the %zu-byte static scratch buffer "
+                        "(call attn_causal_prefill with a workspace instead)",
+                        need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+        if ((st = scratch_address(&workspace))) return st;
+        ws_bytes = (size_t)ATTN_NOALLOC_SCRATCH_BYTES;
+    }
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? ws_bytes : (size_t)0);
@@ -2323,6 +2361,15 @@ int attn_causal_prefill(const void* q, const void* k, const void* v, void* out, 
                         void* stream) {
     return prefill_call(q, k, v, out, B, Hq, Hkv, Lq, Lkv, D, scale, q_str, k_str, v_str, o_str,
                         q_pos0, nullptr, window, workspace, ws_bytes, stream);
+}
+
+int attn_causal_prefill_noalloc(const void* q, const void* k, const void* v, void* out, int B,
+                                int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                                const int64_t q_str[4], const int64_t k_str[4],
+                                const int64_t v_str[4], const int64_t o_str[4], int64_t q_pos0,
+                                int window, void* stream) {
+    return prefill_call(q, k, v, out, B, Hq, Hkv, Lq, Lkv, D, scale, q_str, k_str, v_str, o_str,
+                        q_pos0, nullptr, window, nullptr, 0, stream, true);
 }
 
 size_t attn_causal_prefill_dev_workspace(int B, int Hq, int Hkv, int Lq, int Lkv, int D) {

@@ -111,6 +111,34 @@ int attn_causal_prefill(const void *q, const void *k, const void *v, void *out,
                         void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * attn_causal_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace: the split
+ * partials go to a static device buffer of ATTN_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends.  The
+ * caller still passes inputs and outputs; the computation, the validation
+ * and the launch plan are those of attn_causal_prefill, so the outputs are
+ * the same bits.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device reads the
+ * buffer's device address once.
+ *
+ * Returns ATTN_ERR_WORKSPACE when the call's split partials would exceed
+ * the buffer (attn_causal_prefill_workspace(...) > ATTN_NOALLOC_SCRATCH_BYTES;
+ * e.g. B=1, Hq=16, Hkv=2, Lq=1024, Lkv=131072, D=128 needs about 34 MB).
+ * Every call on a device shares that device's buffer: calls that overlap in
+ * time on one device (other streams, other threads) race and must be
+ * serialised by the caller.  No part of the buffer needs to start at zero,
+ * and each call fully writes what it later reads.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int attn_causal_prefill_noalloc(const void *q, const void *k, const void *v, void *out,
+                                int B, int Hq, int Hkv, int Lq, int Lkv, int D, float scale,
+                                const int64_t q_str[4], const int64_t k_str[4],
+                                const int64_t v_str[4], const int64_t o_str[4],
+                                int64_t q_pos0, int window, void *stream);
+
+/*
  * The same prefill with a device-resident KV bound.
  *
  * Defines ("[CUDA] Use Triton TMA for long-context causal prefill",

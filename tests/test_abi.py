@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -96,6 +96,31 @@ def _prefill(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64, scale=0
 def test_prefill_validation(kw, code):
     assert _prefill(**kw) == code
     assert attn.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), attn.ATTN_ERR_INVALID),
+    (dict(B=0), attn.ATTN_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID),
+    (dict(D=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(qs=_s(4 * 8 * 64, 8 * 64, 64, 2)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(out=A + 8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(Lq=0), attn.ATTN_OK),
+])
+def test_prefill_noalloc_validates_like_prefill(kw, code):
+    """The allocation-free entry point runs the same host validation before
+    any HIP call (and Lq == 0 enqueues nothing)."""
+    L = _lib()
+    a = dict(q=A, k=A, v=A, out=A, B=1, Hq=4, Hkv=2, Lq=8, Lkv=16, D=64)
+    a.update({n: kw[n] for n in a if n in kw})
+    Hq, Hkv, Lq, Lkv, D = a["Hq"], a["Hkv"], a["Lq"], a["Lkv"], a["D"]
+    qs = kw.get("qs") or _s(Hq * Lq * D, Lq * D, D, 1)
+    ks = _s(Hkv * Lkv * D, Lkv * D, D, 1)
+    rc = L.attn_causal_prefill_noalloc(a["q"], a["k"], a["v"], a["out"], a["B"], Hq, Hkv, Lq,
+                                       Lkv, D, 0.125, qs, ks, ks, qs, Lkv - Lq, 0, None)
+    assert rc == code, attn.last_error()
+    assert "ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
+    assert attn.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_prefill_empty_query_is_a_noop():
