@@ -44,6 +44,25 @@ PREFILL_WORKLOADS = {
     "d256_lq512_lkv16k": dict(wid=6, B=1, Hq=16, Hkv=2, D=256, Lq=512, Lkv=16384, q_pos0=None),
 }
 
+# The D=128 long-context chunk with keys that push every workgroup onto the
+# exact softmax rerun (see rising_logits).
+PREFILL_WORKLOADS["d128_lq1k_lkv128k_rising"] = dict(
+    wid=3, B=1, Hq=16, Hkv=2, D=128, Lq=1024, Lkv=131072, q_pos0=None, logits="rising")
+
+
+def rising_logits(q, k, scale, nats, period):
+    """Q made positive and K moved along the all-ones direction so that the
+    logit of key j against the mean query rises by nats * (j mod period) /
+    period: a saw-tooth whose every period rises by `nats`.  Returns (q, k),
+    bf16.  No attention arithmetic: a shift of the inputs only."""
+    qpos = q.abs()
+    qsum = qpos.float().sum(-1).mean().item()
+    Lkv = k.shape[2]
+    ramp = nats * (torch.arange(Lkv, dtype=torch.float32) % period) / period
+    shift = (ramp / (scale * qsum)).view(1, 1, -1, 1)
+    return qpos, (k.float() + shift).to(torch.bfloat16)
+
+
 # Varlen column store of the segment-table workload: [rows, cols, Hkv, D];
 # the last column is scratch.  Packed Q/out are [T, Hq, D].
 VARLEN_STORE = dict(rows=8192, cols=9, Hkv=2, D=128, Hq=16)
