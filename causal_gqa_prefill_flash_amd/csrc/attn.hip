@@ -900,17 +900,30 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
 template <int D, bool PS>
 __device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, float cq) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    const uint32_t flip = cq < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         const uint4 u = valid ? ld16(qrow + 16 * kk + 8 * hh) : make_uint4(0, 0, 0, 0);
         uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        if (PS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)  // bf16 pair: element 0 in the low half
-            w[j] = PS ? pack_bf16x2(__uint_as_float(w[j] << 16) * cq,
-                                    __uint_as_float(w[j] & 0xffff0000u) * cq)
-                      : w[j] ^ flip;
+            for (int j = 0; j < 4; ++j)  // bf16 pair: element 0 in the low half
+                w[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * cq,
+                                   __uint_as_float(w[j] & 0xffff0000u) * cq);
+        }
         qf[kk] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    // exact Q: only a negative scale changes it (its sign, in a uniform
+    // branch), so with a positive scale nothing waits for the loads here
+    if (!PS && cq < 0.f) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 u = __builtin_bit_cast(uint4, qf[kk]);
+            u.x ^= 0x80008000u;
+            u.y ^= 0x80008000u;
+            u.z ^= 0x80008000u;
+            u.w ^= 0x80008000u;
+            qf[kk] = __builtin_bit_cast(bf16x8, u);
+        }
     }
 }
 
@@ -952,6 +965,51 @@ __device__ inline void store_partial(const f32x16* o, float m, float lpart, floa
         pml[0] = l > 0.f ? (m == -INFINITY ? 0.f : m * c) : -INFINITY;
         pml[1] = l;
     }
+}
+
+// Prefill split partial of one row, at half the bytes of store_partial: the
+// accumulator divided by its sum (a convex combination of V rows) and by
+// 2^e, with e the exponent of the row's largest |value| (clamped to
+// [-100, 127]), so every element lies in [-1, 1]; rounded to fp16, where the
+// rounding moves an element by at most 2^-12 of 2^e, i.e. 2^-11 of the row's
+// largest value.  The record pml holds (m c or -inf when nothing was
+// visible, l, l 2^e, 0) in fp32: the merge weighs the fp16 values by l 2^e.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+template <int D>
+__device__ inline void store_partial_h(const f32x16* o, float m, float lpart, float c, u16* po,
+                                       float* pml, bool valid) {
+    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
+    const float l = sum_across_halves(lpart);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fabsf(o[dt][r]));
+    mx = max_across_halves(mx) * inv;
+    int e = 0;
+    (void)frexpf(mx, &e);  // mx < 2^e (e = 0 for mx = 0)
+    e = e < -100 ? -100 : (e > 127 ? 127 : e);
+    const float sc = ldexpf(inv, -e);
+    if (!valid) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int d = 32 * dt + 8 * a + 4 * hh;
+            *reinterpret_cast<uint2*>(po + d) =
+                make_uint2(pack_f16x2(o[dt][4 * a] * sc, o[dt][4 * a + 1] * sc),
+                           pack_f16x2(o[dt][4 * a + 2] * sc, o[dt][4 * a + 3] * sc));
+        }
+    if (hh == 0)
+        *reinterpret_cast<float4*>(pml) =
+            make_float4(l > 0.f ? (m == -INFINITY ? 0.f : m * c) : -INFINITY, l, ldexpf(l, e), 0.f);
 }
 
 template <int D>
@@ -1058,8 +1116,8 @@ struct PrefillArgs {
     const u16* k;
     const u16* v;
     u16* out;
-    float* part_o;   // [nsplit][B][Hq][Lq][D]
-    float* part_ml;  // [nsplit][B][Hq][Lq][2]
+    u16* part_o;     // [nsplit][B][Hq][Lq][D] fp16 bits (store_partial_h)
+    float* part_ml;  // [nsplit][B][Hq][Lq][4]
     int B, Hq, Hkv, Lq, Lkv, window, nsplit;
     int n_inner;  // q blocks x head chunks
     float c;  // |scale| * log2(e)
@@ -1167,8 +1225,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                          valid[nt]);
         } else {
             const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[nt]) * a.Lq + irow[nt];
-            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
-                             a.part_ml + row * 2, valid[nt]);
+            store_partial_h<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
+                               a.part_ml + row * 4, valid[nt]);
         }
     }
     clock_add(a.clk, cm);
@@ -1353,8 +1411,8 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
     } else {
         const int64_t row =
             (((int64_t)split * a.B + b) * a.Hq + hrow) * a.Lq + irow;
-        store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 2,
-                         valid);
+        store_partial_h<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
+                           valid);
     }
     clock_add(a.clk, cm);
 }
@@ -1407,6 +1465,54 @@ __device__ inline void combine_row(const float* po, const float* pml, int64_t sp
     *reinterpret_cast<uint2*>(orow + d0) = o;
 }
 
+// combine_row for the fp16 partials of store_partial_h: split s contributes
+// 2^(m_s - M) l_s 2^e_s times its fp16 values to the numerator and
+// 2^(m_s - M) l_s to the denominator.
+template <int D, int G = 8>
+__device__ inline void combine_row_h(const u16* po, const float* pml, int64_t split_stride_o,
+                                     int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
+    float M = -INFINITY, L = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += G) {
+        float4 r[G];
+        uint2 x[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int sj = min(s0 + j, nsplit - 1);
+            r[j] = *reinterpret_cast<const float4*>(pml + sj * split_stride_ml);
+            x[j] = *reinterpret_cast<const uint2*>(po + sj * split_stride_o + d0);
+        }
+        float Mg = M;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (s0 + j < nsplit) Mg = __builtin_fmaxf(Mg, r[j].x);
+        if (Mg == -INFINITY) continue;  // nothing visible so far
+        const float rs = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
+        L *= rs;
+        acc[0] *= rs;
+        acc[1] *= rs;
+        acc[2] *= rs;
+        acc[3] *= rs;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float w = (s0 + j < nsplit && r[j].x != -INFINITY)
+                                ? __builtin_amdgcn_exp2f(r[j].x - Mg) : 0.f;
+            const f16x2 lo = __builtin_bit_cast(f16x2, x[j].x), hi = __builtin_bit_cast(f16x2, x[j].y);
+            const float wz = w * r[j].z;
+            L += w * r[j].y;
+            acc[0] += wz * (float)lo[0];
+            acc[1] += wz * (float)lo[1];
+            acc[2] += wz * (float)hi[0];
+            acc[3] += wz * (float)hi[1];
+        }
+        M = Mg;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    *reinterpret_cast<uint2*>(orow + d0) = o;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     constexpr int TPR = D / 4;  // threads per row, 4 dims each
@@ -1421,11 +1527,11 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     // loads of every split in flight at once, in the narrowest group that
     // holds them (no clamped duplicates)
     if (a.nsplit <= 4)
-        combine_row<D, 4>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit,
-                          d0, orow);
+        combine_row_h<D, 4>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
+                            d0, orow);
     else
-        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 2, rows * D, rows * 2, a.nsplit,
-                          d0, orow);
+        combine_row_h<D, 8>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
+                            d0, orow);
 }
 
 // ---------------------------------------------------------------- varlen
@@ -1533,11 +1639,12 @@ __device__ inline SegPlan seg_plan(const Segment& g, int P, int hg, int gq, int 
     int64_t lo, hi, pmn, pmx, lo1, hi1;
     block_range(g, 0, Pb, &lo, &hi, &pmn, &pmx);
     block_range(g, p.nqb - 1, Pb, &lo1, &hi1, &pmn, &pmx);
-    const int64_t span = max(hi - lo, hi1 - lo1);
-    const int64_t n = (span + split_keys - 1) / split_keys;
-    p.nsplit = n < 1 ? 1 : (n > nsplit_max ? nsplit_max : (int)n);
-    const int64_t tiles = ((span + p.nsplit - 1) / p.nsplit + kBN - 1) / kBN;
-    p.cost = (int)min((int64_t)0x3fffffff, p.decode ? (tiles + kWaves - 1) / kWaves + 1 : tiles);
+    // a range lies inside [0, kv_end), kv_end < 2^31: 32-bit divisions
+    const unsigned span = (unsigned)max(hi - lo, hi1 - lo1);
+    const unsigned n = (span + (unsigned)split_keys - 1u) / (unsigned)split_keys;
+    p.nsplit = n < 1u ? 1 : (n > (unsigned)nsplit_max ? nsplit_max : (int)n);
+    const unsigned tiles = (span / (unsigned)p.nsplit + (span % (unsigned)p.nsplit != 0) + kBN - 1) / kBN;
+    p.cost = (int)min(0x3fffffffu, p.decode ? (tiles + kWaves - 1) / kWaves + 1 : tiles);
     p.count = p.decode ? hkv * p.nsplit : p.nqb * hg * p.nsplit;
     return p;
 }
@@ -2141,10 +2248,11 @@ int prefill_splits(int B, int Hq, int Hkv, int Lq, int Lkv, int D, const DeviceI
     return ns;
 }
 
+// Prefill split partials: fp16 values (D per row) and a 4-float record per row.
 size_t prefill_ws_bytes(int B, int Hq, int Lq, int D, int nsplit) {
     if (nsplit <= 1) return 0;
     size_t rows = (size_t)nsplit * B * Hq * Lq;
-    return align256(rows * D * sizeof(float)) + align256(rows * 2 * sizeof(float));
+    return align256(rows * D * sizeof(u16)) + align256(rows * 4 * sizeof(float));
 }
 
 // Target keys per split of a varlen q-block (ATTN_VARLEN_SPLIT_KEYS overrides,
@@ -2282,9 +2390,9 @@ static int prefill_call(const void* q, const void* k, const void* v, void* out, 
     a.out = (u16*)out;
     size_t prow = (size_t)nsplit * B * Hq * Lq;
     const bool parts = need > errb;
-    a.part_o = parts ? (float*)((char*)workspace + errb) : nullptr;
+    a.part_o = parts ? (u16*)((char*)workspace + errb) : nullptr;
     a.part_ml =
-        parts ? (float*)((char*)workspace + errb + align256(prow * D * sizeof(float))) : nullptr;
+        parts ? (float*)((char*)workspace + errb + align256(prow * D * sizeof(u16))) : nullptr;
     a.bounds = bounds;
     a.err = bounds ? (int32_t*)workspace : nullptr;
     a.B = B;

@@ -255,3 +255,20 @@ def test_windowed_rows_with_very_negative_logits():
     ref = oracle.prefill(q, k, v, scale, window=64)
     compare(out, ref, "windowed negative logits")
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("shift", [-20, 20])
+def test_split_partials_hold_any_magnitude(D, shift, monkeypatch):
+    """Split partials are kept in fp16 with a per-row power-of-two scale: V
+    scaled by 2^shift (beyond fp16's range either way) gives the unscaled
+    result scaled by 2^shift, within the bar once scaled back, with five
+    forced key splits."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", "5")
+    B, Hq, Hkv, Lq, Lkv = 1, 8, 2, 150, 2500
+    say("split partials, V x 2^%d, D %d" % (shift, D))
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=28)
+    vs = (v.float() * 2.0 ** shift).to(torch.bfloat16)  # exact: a power of two
+    out = _run(q, k, vs)
+    ref = oracle.prefill(q, k, v, 1.0 / math.sqrt(D))
+    compare(out.float() * 2.0 ** -shift, ref, "V x 2^%d D %d" % (shift, D))
