@@ -945,30 +945,8 @@ __device__ inline void store_out(const f32x16* o, float lpart, u16* orow, bool v
         }
 }
 
-// Split partial of one row: unnormalised accumulator, log2-domain maximum
-// (m*c, -inf when nothing was visible) and the sum.
-template <int D>
-__device__ inline void store_partial(const f32x16* o, float m, float lpart, float c, float* po,
-                                     float* pml, bool valid) {
-    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    const float l = sum_across_halves(lpart);
-    if (!valid) return;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int d = 32 * dt + 8 * a + 4 * hh;
-            *reinterpret_cast<float4*>(po + d) =
-                make_float4(o[dt][4 * a], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]);
-        }
-    if (hh == 0) {
-        pml[0] = l > 0.f ? (m == -INFINITY ? 0.f : m * c) : -INFINITY;
-        pml[1] = l;
-    }
-}
-
-// Prefill split partial of one row, at half the bytes of store_partial: the
-// accumulator divided by its sum (a convex combination of V rows) and by
+// Split partial of one row (prefill and varlen), at half the bytes of fp32:
+// the accumulator divided by its sum (a convex combination of V rows) and by
 // 2^e, with e the exponent of the row's largest |value| (clamped to
 // [-100, 127]), so every element lies in [-1, 1]; rounded to fp16, where the
 // rounding moves an element by at most 2^-12 of 2^e, i.e. 2^-11 of the row's
@@ -982,7 +960,7 @@ __device__ inline uint32_t pack_f16x2(float a, float b) {
 }
 
 template <int D>
-__device__ inline void store_partial_h(const f32x16* o, float m, float lpart, float c, u16* po,
+__device__ inline void store_partial(const f32x16* o, float m, float lpart, float c, u16* po,
                                        float* pml, bool valid) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
     const float l = sum_across_halves(lpart);
@@ -1116,7 +1094,7 @@ struct PrefillArgs {
     const u16* k;
     const u16* v;
     u16* out;
-    u16* part_o;     // [nsplit][B][Hq][Lq][D] fp16 bits (store_partial_h)
+    u16* part_o;     // [nsplit][B][Hq][Lq][D] fp16 bits (store_partial)
     float* part_ml;  // [nsplit][B][Hq][Lq][4]
     int B, Hq, Hkv, Lq, Lkv, window, nsplit;
     int n_inner;  // q blocks x head chunks
@@ -1225,7 +1203,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                          valid[nt]);
         } else {
             const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[nt]) * a.Lq + irow[nt];
-            store_partial_h<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
+            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
                                a.part_ml + row * 4, valid[nt]);
         }
     }
@@ -1411,65 +1389,20 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
     } else {
         const int64_t row =
             (((int64_t)split * a.B + b) * a.Hq + hrow) * a.Lq + irow;
-        store_partial_h<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
+        store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
                            valid);
     }
     clock_add(a.clk, cm);
 }
 
-// Merge split partials of one row: M = max m_s, w_s = 2^(m_s - M),
-// o = sum_s w_s acc_s / sum_s w_s l_s (0 when the sum is 0).  The splits are
-// read in groups of G whose loads are all in flight together (indices past
-// nsplit are clamped and weighted 0); groups merge by the same rule.
+// Merge the split partials (store_partial) of one row: M = max m_s, w_s =
+// 2^(m_s - M); split s adds w_s l_s 2^e_s times its fp16 values to the
+// numerator and w_s l_s to the denominator; o = numerator / denominator (0
+// when it is 0).  The splits are read in groups of G whose loads are all in
+// flight together (indices past nsplit are clamped and weighted 0); groups
+// merge by the same rule.
 template <int D, int G = 8>
-__device__ inline void combine_row(const float* po, const float* pml, int64_t split_stride_o,
-                                   int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
-    float M = -INFINITY, L = 0.f;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += G) {
-        float m[G], l[G];
-        float4 x[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int sj = min(s0 + j, nsplit - 1);
-            m[j] = pml[sj * split_stride_ml];
-            l[j] = pml[sj * split_stride_ml + 1];
-            x[j] = *reinterpret_cast<const float4*>(po + sj * split_stride_o + d0);
-        }
-        float Mg = M;
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-            if (s0 + j < nsplit) Mg = __builtin_fmaxf(Mg, m[j]);
-        if (Mg == -INFINITY) continue;  // nothing visible so far
-        const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
-        L *= r;
-        acc[0] *= r;
-        acc[1] *= r;
-        acc[2] *= r;
-        acc[3] *= r;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float w = (s0 + j < nsplit && m[j] != -INFINITY)
-                                ? __builtin_amdgcn_exp2f(m[j] - Mg) : 0.f;
-            L += w * l[j];
-            acc[0] += w * x[j].x;
-            acc[1] += w * x[j].y;
-            acc[2] += w * x[j].z;
-            acc[3] += w * x[j].w;
-        }
-        M = Mg;
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
-    *reinterpret_cast<uint2*>(orow + d0) = o;
-}
-
-// combine_row for the fp16 partials of store_partial_h: split s contributes
-// 2^(m_s - M) l_s 2^e_s times its fp16 values to the numerator and
-// 2^(m_s - M) l_s to the denominator.
-template <int D, int G = 8>
-__device__ inline void combine_row_h(const u16* po, const float* pml, int64_t split_stride_o,
+__device__ inline void combine_row(const u16* po, const float* pml, int64_t split_stride_o,
                                      int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
     float M = -INFINITY, L = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1527,10 +1460,10 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     // loads of every split in flight at once, in the narrowest group that
     // holds them (no clamped duplicates)
     if (a.nsplit <= 4)
-        combine_row_h<D, 4>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
+        combine_row<D, 4>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
                             d0, orow);
     else
-        combine_row_h<D, 8>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
+        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
                             d0, orow);
 }
 
@@ -1544,8 +1477,8 @@ struct VarlenArgs {
     const int32_t* seq_info;
     const int32_t* seg_attr;
     int32_t* err;    // one word per finish workgroup
-    float* part_o;   // split partials per packed row: [T][Hq][nsplit][D]
-    float* part_ml;  // [T][Hq][nsplit][2]
+    u16* part_o;     // split partials per packed row: [T][Hq][nsplit][D], fp16 bits
+    float* part_ml;  // [T][Hq][nsplit][4] (store_partial records)
     int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows;
     int nsplit;      // most key splits of a q-block
     int split_keys;  // target keys per split
@@ -1841,6 +1774,24 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
 #pragma unroll
         for (int j = 0; j < RPW; ++j) acc[j] += obv[(w * RPW + j) * kWave + lane];
     }
+    // a split partial takes the format of store_partial: the row's largest
+    // |value| over all waves (each holds RPW of a lane's registers) sets the
+    // power-of-two scale
+    int e = 0;
+    if (nsplit > 1) {
+        __shared__ float sh_x[kWaves][32];
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(acc[j]));
+        mx = max_across_halves(mx);
+        if (lane < 32) sh_x[w][lane] = mx;
+        __syncthreads();
+        mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) mx = __builtin_fmaxf(mx, sh_x[v][r]);
+        (void)frexpf(L > 0.f ? mx / L : 0.f, &e);
+        e = e < -100 ? -100 : (e > 127 ? 127 : e);
+    }
     if (!valid) return;
     // register ri = dt*16 + i of a lane holds d = 32dt + 8(i/4) + 4hh + i%4
     if (nsplit == 1) {
@@ -1856,17 +1807,19 @@ __device__ __forceinline__ void decode_item(const VarlenArgs& a, const Segment& 
         }
     } else {
         const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit + split;
-        float* po = a.part_o + row * D;
+        u16* po = a.part_o + row * D;
+        const float sc = ldexpf(L > 0.f ? 1.f / L : 0.f, -e);
 #pragma unroll
         for (int j = 0; j < RPW; j += 4) {
             const int ri = w * RPW + j, dt = ri / 16, i = ri % 16;
             const int d = 32 * dt + 8 * (i / 4) + 4 * hh;
-            *reinterpret_cast<float4*>(po + d) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+            *reinterpret_cast<uint2*>(po + d) =
+                make_uint2(pack_f16x2(acc[j] * sc, acc[j + 1] * sc),
+                           pack_f16x2(acc[j + 2] * sc, acc[j + 3] * sc));
         }
-        if (w == 0 && hh == 0) {
-            a.part_ml[row * 2] = L > 0.f ? mref * c : -INFINITY;
-            a.part_ml[row * 2 + 1] = L;
-        }
+        if (w == 0 && hh == 0)
+            *reinterpret_cast<float4*>(a.part_ml + row * 4) =
+                make_float4(L > 0.f ? mref * c : -INFINITY, L, ldexpf(L, e), 0.f);
     }
 }
 
@@ -1950,7 +1903,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
         } else {
             const int64_t row = ((int64_t)t * a.Hq + hrow[nt]) * a.nsplit + split;
             store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
-                             a.part_ml + row * 2, valid[nt]);
+                               a.part_ml + row * 4, valid[nt]);
         }
     }
     clock_add(a.clk, cm);
@@ -2005,11 +1958,11 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
                     // all of a row's loads in flight at once, in the narrower
                     // group when it holds every split
                     if (ns > 8)
-                        combine_row<D, kMaxVarlenSplits>(a.part_o + row * D, a.part_ml + row * 2,
-                                                         D, 2, ns, d0, orow);
+                        combine_row<D, kMaxVarlenSplits>(a.part_o + row * D,
+                                                           a.part_ml + row * 4, D, 4, ns, d0, orow);
                     else
-                        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 2, D, 2, ns, d0,
-                                          orow);
+                        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0,
+                                            orow);
                 }
             }
         }
@@ -2282,7 +2235,7 @@ size_t varlen_ws_bytes(int S, int T, int Hq, int Hkv, int D, int rows) {
     size_t bytes = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
     if (ns > 1) {
         size_t prow = (size_t)(T > 0 ? T : 0) * Hq * ns;
-        bytes += align256(prow * D * sizeof(float)) + align256(prow * 2 * sizeof(float));
+        bytes += align256(prow * D * sizeof(u16)) + align256(prow * 4 * sizeof(float));
     }
     return bytes;
 }
@@ -2577,11 +2530,12 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     a.seg_attr = seg_attr;
     a.err = (int32_t*)workspace;
     size_t errb = align256((size_t)varlen_finish_blocks(T) * sizeof(int32_t));
-    a.part_o = a.part_ml = nullptr;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
     if (nsplit > 1) {
         const size_t prow = (size_t)T * Hq * nsplit;
-        a.part_o = (float*)((char*)workspace + errb);
-        a.part_ml = (float*)((char*)workspace + errb + align256(prow * D * sizeof(float)));
+        a.part_o = (u16*)((char*)workspace + errb);
+        a.part_ml = (float*)((char*)workspace + errb + align256(prow * D * sizeof(u16)));
     }
     a.S = S;
     a.T = T;

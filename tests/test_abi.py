@@ -200,8 +200,9 @@ def test_oracle_rejects_what_the_library_calls_invalid_varlen(kw):
 
 
 def test_varlen_workspace_follows_rows_and_packed_rows():
-    """Error words for T rows, then fp32 split partials per packed row: nsplit
-    = min(16, ceil(rows / 512)) splits of (D + 2) floats for each of Hq heads."""
+    """Error words for T rows, then split partials per packed row: nsplit =
+    min(16, ceil(rows / 512)) splits of D fp16 values and a 4-float record for
+    each of Hq heads."""
     L = _lib()
 
     def al(n):
@@ -209,7 +210,7 @@ def test_varlen_workspace_follows_rows_and_packed_rows():
 
     def expect(T, Hq, D, rows):
         ns = min(16, (rows + 511) // 512)
-        part = al(T * Hq * ns * D * 4) + al(T * Hq * ns * 2 * 4) if ns > 1 else 0
+        part = al(T * Hq * ns * D * 2) + al(T * Hq * ns * 4 * 4) if ns > 1 else 0
         return al(max(T, 1) * 4) + part
 
     a = L.attn_sdpa_varlen_workspace(8, 1727, 16, 2, 128, 8192, 9)

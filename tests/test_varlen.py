@@ -290,3 +290,20 @@ def test_ring_segments_past_their_span_are_flagged(D):
     compare(out, ref, "ring span D%d" % D)
     assert torch.count_nonzero(out[:544]) == 0
     assert torch.count_nonzero(out[550:1062]) > 0
+
+
+@pytest.mark.parametrize("shift", [-20, 20])
+def test_split_partials_hold_any_magnitude(shift):
+    """Varlen split partials (compute and decode items) are fp16 with a
+    per-row power-of-two scale: V scaled by 2^shift, beyond fp16's range
+    either way, gives the unscaled result scaled by 2^shift."""
+    say("varlen split partials, V x 2^%d" % shift)
+    rows, cols, Hkv, D, Hq = 8192, 5, 2, 128, 16
+    info = torch.tensor([(0, 1, 0, 8192), (3, 4, 1, 6000), (10, 16, 2, 7000), (30, 64, 3, 5000)],
+                        dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(96, rows, cols, Hkv, D, Hq, wid=52)
+    vsc = (vs.float() * 2.0 ** shift).to(torch.bfloat16)  # exact: a power of two
+    out, err = _gpu_varlen(q, ks, vsc, info)
+    ref = oracle.varlen(q, ks, vs, info)
+    assert err == 0
+    compare(out.float() * 2.0 ** -shift, ref, "varlen V x 2^%d" % shift)
