@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libattn.so")
+# ATTN_LIB_PATH selects another build of the same library (the host
+# sanitizer build, libattn_san.so, for tests/sanitize.py)
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(_HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 SEG_QRANGE, SEG_COL, SEG_KVEND, SEG_ATTR, SEG_OVERLAP, SEG_SPAN = 1, 2, 4, 8, 16, 32

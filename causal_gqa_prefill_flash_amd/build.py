@@ -21,9 +21,20 @@ def hipcc_cmd(out, extra=()):
              "-I", os.path.join(_ROOT, "include"), "-o", out] + list(extra) + SOURCES)
 
 
-def build(verbose=False, extra=()):
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = hipcc_cmd(tmp, extra)
+LIB_SAN = os.path.join(_HERE, "libattn_san.so")
+# host code only (validation, planning, the C ABI): the device code is built
+# as usual; each -fsanitize= goes to the host pass alone
+SANITIZE_HOST = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+                 "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libsan"]
+
+
+def build(verbose=False, extra=(), sanitize=False):
+    """sanitize: build libattn_san.so, whose host code carries AddressSanitizer
+    and UndefinedBehaviorSanitizer (see tests/sanitize.py)."""
+    out = LIB_SAN if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = hipcc_cmd(tmp, list(extra) + (SANITIZE_HOST if sanitize else []))
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,9 +44,9 @@ def build(verbose=False, extra=()):
         print("\n".join(msgs), file=sys.stderr)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed (%d)" % r.returncode)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB_PATH selects another build (liboracle_san.so, for tests/sanitize.py)
+_LIB_PATH = os.environ.get("ORACLE_LIB_PATH") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # Bit meanings of the varlen segment flags (the same as the library's error word).
