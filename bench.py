@@ -488,7 +488,9 @@ def bench_kv_write(args, name):
             "roofline": {"bound": "hbm", "achieved": round((wbytes + abytes) / (ms * 1e-3) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round((wbytes + abytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": None, "algorithmic_bytes_per_launch": wbytes + abytes},
+                         # counter bytes of the step's dominant kernel, the attention
+                         "traffic": traffic_from_profile(name), "kernel": "varlen_kernel<%d>" % D,
+                         "algorithmic_bytes_per_launch": wbytes + abytes},
         }
     gbs = wbytes / (ms * 1e-3) / 1e9
     return {
@@ -501,7 +503,8 @@ def bench_kv_write(args, name):
         "config": {"workload": name, "rows": rows, "cols": cols, "Hkv": Hkv, "D": D,
                    "step_tokens": n, "store_copies_rotated": ncopy},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profile(name),
                      "algorithmic_bytes_per_launch": wbytes,
                      "kernel": "kv_write_kernel"},
     }
