@@ -81,6 +81,8 @@ def lib():
     L.attn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
     L.attn_timing_clock.restype = I
     L.attn_timing_clock.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.attn_timing_reruns.restype = I
+    L.attn_timing_reruns.argtypes = [ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_longlong)]
     _lib = L
     return L
 
@@ -334,6 +336,14 @@ def timing_clock():
     mhz, per = ctypes.c_double(0.0), (ctypes.c_double * 8)()
     _check(lib().attn_timing_clock(ctypes.byref(mhz), per))
     return mhz.value, list(per)
+
+
+def timing_reruns():
+    """After ``timing_end``: (attention workgroups that finished, how many of
+    them redid their key range with the exact running maximum)."""
+    n, r = ctypes.c_longlong(0), ctypes.c_longlong(0)
+    _check(lib().attn_timing_reruns(ctypes.byref(n), ctypes.byref(r)))
+    return n.value, r.value
 
 
 def kv_write_workspace_bytes(T):

@@ -13,7 +13,10 @@
 // it, with no per-tile maxima and no rescales.  Softmax does not depend on
 // the reference, so this is exact while nothing overflows or underflows;
 // every row checks its sum afterwards, and a workgroup with a row outside
-// [2^-64, 2^64] redoes its range with the exact running maximum.
+// [2^-64, 2^64] redoes its range with the exact running maximum.  The D = 128
+// prefill kernel also moves a row's reference up, exactly, on every third
+// tile when its sum has passed 2^16, so that logits rising along the keys
+// stay in range.
 //
 // Work decomposition (D = 64, 128: one workgroup = 8 waves = 256 query rows):
 //   rows of a workgroup = (query heads of one KV head) x (query positions);
@@ -723,15 +726,65 @@ __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[
     pin_m_outputs<D>(S, st, QK, PV);
 }
 
+// Refresh of the fixed references in the fixed-reference pass when the
+// scores come out of the MFMAs relative to them (scale in Q): on every
+// third tile, before its P, a row whose running sum lies in (2^16, 2^64]
+// moves its reference up by d = floor(log2 l).  Its l and O are multiplied
+// by 2^-d, which is exact (a power of two), the current tile's scores lose
+// d, and later tiles start from the new reference.  Softmax does not depend
+// on the reference, so this changes only the range: when the logits rise
+// along the keys (by up to about 0.2 in log2 units per key on average over
+// three tiles), the sums stay below 2^64 instead of overflowing it, which
+// would send the workgroup to the pass with the exact running maximum.  A
+// row above 2^64 is left alone (its P may already have lost range), so the
+// check after the pass still sees it: a sum only grows between refreshes.
+// Sums that are too small need nothing: they only grow, and the terms that
+// underflowed are negligible next to a final sum of at least 2^-64.  A wave
+// with no lane share above 2^16 pays a compare.
+constexpr float kRefreshHi = 0x1p16f;
+template <int D>
+constexpr bool kRefresh = D == 128;  // D = 64: the softmax phase is the bound
+
+template <int D>
+__device__ inline void refresh_reference(TileScores& s, RowState<D>& st) {
+    bool out = false;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) out |= st.l[nt] > kRefreshHi;
+    if (__builtin_expect(!__any(out), 1)) return;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float lrow = sum_across_halves(st.l[nt]);
+        const bool move = lrow > kRefreshHi && lrow <= 0x1p64f;
+        // floor(log2 lrow) from the exponent field, 16 <= d <= 64
+        const int d = move ? __builtin_amdgcn_frexp_expf(lrow) - 1 : 0;
+        const float df = (float)d;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[nt][t][r] -= df;
+        const float ref = (st.m[nt] == -INFINITY ? 0.f : st.m[nt]) + df;
+        st.m[nt] = move ? ref : st.m[nt];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.mneg[nt][r] = move ? -ref : st.mneg[nt][r];
+        st.l[nt] = __builtin_amdgcn_ldexpf(st.l[nt], -d);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                st.o[nt][dt][r] = __builtin_amdgcn_ldexpf(st.o[nt][dt][r], -d);
+    }
+}
+
 // VALU phase of a wave for tile k: mask (edge tiles), then P(k) and its row
 // sums.  EXACT: against each row's running maximum, with the rescale of O
 // and l when it moves.  Otherwise against the row's fixed reference st.m (0
 // while it is -inf), with no maxima and no rescale; the caller checks
 // afterwards that every row's sum stayed in range.
-template <int D, bool EXACT, bool PRE, class KV>
+template <int D, bool EXACT, bool PRE, class KV, bool REF = false>
 __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const LaneBounds* lb,
                                TileScores& S, TileP& pk, RowState<D>& st) {
     if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
+    if (REF && PRE && !EXACT) refresh_reference<D>(S, st);
     if (EXACT) {
         float alpha[kNT];
         update_max(S, c, st.m, alpha);
@@ -775,7 +828,7 @@ __device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L,
 // softmax phase also prepares the next step's copy descriptors (K(k+3) into
 // Kn, V(k+2) into Vn): scalar work that would otherwise delay the first
 // MFMA of the next phase.
-template <int D, bool EXACT, bool PRE, class KV>
+template <int D, bool EXACT, bool PRE, class KV, bool REF = false>
 __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
                                float c, const LaneBounds* lb, TileScores& S, TileP& pk,
                                RowState<D>& st, const u16* Kr, const u16* Vr,
@@ -784,7 +837,7 @@ __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf
     typedef typename TileCopySel<D, KV>::T TC;
     m_phase<D, true, true, PRE>(Kr, Vr, qf, S, pk, st, ck, cv);
     copy_wait_barrier<2 * TC::N>();
-    v_phase<D, EXACT, PRE>(L, k, c, lb, S, pk, st);
+    v_phase<D, EXACT, PRE, KV, REF>(L, k, c, lb, S, pk, st);
     ck = k_copy<D>(L, k + 3, Kn);
     cv = v_copy<D>(L, k + 2, Vn);
     phase_barrier();
@@ -867,8 +920,8 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
         pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
         pp_step<D, EXACT, PRE>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
                           sm.v[1]);
-        pp_step<D, EXACT, PRE>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck, cv, sm.k[0],
-                          sm.v[2]);
+        pp_step<D, EXACT, PRE, KV, kRefresh<D>>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck,
+                                              cv, sm.k[0], sm.v[2]);
     }
     if (k < n) {
         pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
@@ -1025,7 +1078,7 @@ __device__ inline void split_range(int lo_all, int hi_all, int split, int nsplit
 //   pass then starts its score MFMAs from the negated references
 //   (set_reference) and takes 2^s directly.
 template <int D, bool PS, class KV>
-__device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
+__device__ bool attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
                        const int64_t* p_lane, int64_t p_min, int64_t p_max,
                        const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
                        const TileSmem<D>& sm) {
@@ -1041,11 +1094,11 @@ __device__ void attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
     }
     if (__any(bad) && (threadIdx.x & (kWave - 1)) == 0) *sm.rerun = 1;
     __syncthreads();
-    if (*sm.rerun) {
-        init_state<D>(st);
-        attend_range<D, true, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c,
-                                     st, sm);
-    }
+    if (!*sm.rerun) return false;
+    init_state<D>(st);
+    attend_range<D, true, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
+                                 sm);
+    return true;
 }
 
 // ---------------------------------------------------------------- prefill
@@ -1059,8 +1112,10 @@ constexpr int64_t kBoundPos = (int64_t)1 << 62;
 // counter (s_memrealtime) when it starts and when it is done, and adds both
 // lifetimes to the sums of its XCD: clk[2x] shader cycles, clk[2x+1]
 // reference ticks.  The ratio is the average shader clock while the
-// workgroups ran.  clk is null unless timing is on.
-__device__ unsigned long long g_clock[16];
+// workgroups ran.  clk[16] counts the workgroups that added to the sums and
+// clk[17] those among them whose fixed-reference pass had to be redone with
+// the exact running maximum.  clk is null unless timing is on.
+__device__ unsigned long long g_clock[18];
 
 struct ClockMark {
     unsigned long long cyc, ref;
@@ -1075,7 +1130,7 @@ __device__ inline ClockMark clock_mark(const unsigned long long* clk) {
     return m;
 }
 
-__device__ inline void clock_add(unsigned long long* clk, ClockMark m) {
+__device__ inline void clock_add(unsigned long long* clk, ClockMark m, bool redone = false) {
     if (clk) {
         const unsigned long long cyc = __builtin_amdgcn_s_memtime();
         const unsigned long long ref = __builtin_amdgcn_s_memrealtime();
@@ -1085,6 +1140,8 @@ __device__ inline void clock_add(unsigned long long* clk, ClockMark m) {
         if (threadIdx.x == 0) {  // vector atomics from one lane
             atomicAdd(clk + 2 * xcc, cyc - m.cyc);
             atomicAdd(clk + 2 * xcc + 1, ref - m.ref);
+            atomicAdd(clk + 16, 1ull);
+            if (redone) atomicAdd(clk + 17, 1ull);
         }
     }
 }
@@ -1192,7 +1249,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     KVFlat kv{a.k + b * a.ks[0] + hk * a.ks[1], a.v + b * a.vs[0] + hk * a.vs[1], a.ks[2],
               a.vs[2]};
     const float c = PS ? 1.f : a.c;
-    attend<D, PS>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, c, st, sm);
+    const bool redone = attend<D, PS>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1207,7 +1264,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                                a.part_ml + row * 4, valid[nt]);
         }
     }
-    clock_add(a.clk, cm);
+    clock_add(a.clk, cm, redone);
 }
 
 // ---------------------------------------------------------------- D = 256
@@ -1326,6 +1383,7 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
 
     RowState<D> st;
     init_state<D>(st);
+    bool redone = false;
     if (k_lo < k_hi) {
         const int n = (k_hi - k_lo + kBN - 1) / kBN;
         // tiles t_in0 <= t < t_in1 need no mask (as interior_tiles)
@@ -1367,7 +1425,8 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         const bool bad = lb.lo < k_hi && !(lrow >= 0x1p-64f && lrow <= 0x1p64f);
         if (__any(bad) && lane == 0) rerun = 1;
         __syncthreads();
-        if (rerun) {
+        redone = rerun != 0;
+        if (redone) {
             init_state<D>(st);
             copy_tile256(kb, a.ks[2], kco, k_lo, k_hi, sk0);
             copy_tile256(vb, a.vs[2], vco, k_lo, k_hi, sv0);
@@ -1392,7 +1451,7 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
                            valid);
     }
-    clock_add(a.clk, cm);
+    clock_add(a.clk, cm, redone);
 }
 
 // Merge the split partials (store_partial) of one row: M = max m_s, w_s =
@@ -1892,7 +1951,8 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     KVRing kv{a.k + (int64_t)sg.col * a.ks[1] + (int64_t)hk * a.ks[2],
               a.v + (int64_t)sg.col * a.vs[1] + (int64_t)hk * a.vs[2], a.ks[0], a.vs[0], sg.R,
               0xFFFFFFFFu / (unsigned)sg.R};
-    attend<D, false>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
+    const bool redone =
+        attend<D, false>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -1906,7 +1966,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
                                a.part_ml + row * 4, valid[nt]);
         }
     }
-    clock_add(a.clk, cm);
+    clock_add(a.clk, cm, redone);
 }
 
 // Finish pass, one packed row per workgroup: merge split partials, zero a
@@ -2757,6 +2817,25 @@ int attn_timing_clock(double* mhz, double xcd_mhz[8]) {
     }
     if (ref <= 0.0) return fail(ATTN_ERR_HIP, "no clock sums were recorded");
     *mhz = 100.0 * cyc / ref;
+    return ATTN_OK;
+}
+
+int attn_timing_reruns(long long* workgroups, long long* redone) {
+    clear_err();
+    if (!workgroups || !redone) return fail(ATTN_ERR_INVALID, "null output pointer");
+    *workgroups = 0;
+    *redone = 0;
+    if (g_timing.on) return fail(ATTN_ERR_INVALID, "timing is still on (call attn_timing_end first)");
+    if (!g_timing.clk) return fail(ATTN_ERR_HIP, "no clock sums were recorded");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipSetDevice(g_timing.dev) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "could not select the timed device");
+    unsigned long long h[2];
+    hipError_t e = hipMemcpy(h, g_timing.clk + 16, sizeof h, hipMemcpyDeviceToHost);
+    (void)hipSetDevice(cur);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "copy of the workgroup counts failed");
+    *workgroups = (long long)h[0];
+    *redone = (long long)h[1];
     return ATTN_OK;
 }
 

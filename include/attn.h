@@ -296,7 +296,7 @@ int attn_kv_write_read_error(const void *workspace, int T, void *stream, int32_t
  * kernel (the split-merge and finish kernels are not included), and the
  * attention kernels launched on the device that was current at
  * attn_timing_begin() add their workgroups' lifetimes, in shader cycles and
- * in the 100 MHz reference clock, to per-XCD sums held in a 128-byte static
+ * in the 100 MHz reference clock, to per-XCD sums held in a 144-byte static
  * device array (no allocation).  attn_timing_begin() clears those sums and
  * synchronises the device; call it outside graph capture.
  *
@@ -314,6 +314,19 @@ int attn_kv_write_read_error(const void *workspace, int T, void *stream, int32_t
 int attn_timing_begin(void);
 int attn_timing_end(double *kernel_ms, int *launches);
 int attn_timing_clock(double *mhz, double xcd_mhz[8]);
+
+/*
+ * attn_timing_reruns(), after attn_timing_end(), writes how many attention
+ * workgroups of the timed launches finished (*workgroups; workgroups of a
+ * varlen launch that found no work are not counted) and how many of them
+ * found a row sum outside [2^-64, 2^64] after the pass with fixed softmax
+ * references and redid their key range with the exact running maximum
+ * (*redone).  The counts come from the same static device array as the
+ * clock sums.  Returns ATTN_ERR_INVALID while timing is on or for null
+ * outputs, ATTN_ERR_HIP when nothing was recorded or the counts could not
+ * be read.
+ */
+int attn_timing_reruns(long long *workgroups, long long *redone);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     assert L.attn_abi_version() == 1
@@ -299,6 +299,18 @@ def test_timing_clock_needs_recorded_sums():
     # no attention kernel ran, so there are no sums: an error, outputs cleared
     assert L.attn_timing_clock(ctypes.byref(mhz), per) == attn.ATTN_ERR_HIP
     assert mhz.value == 0.0 and list(per) == [0.0] * 8
+
+
+def test_timing_reruns_rejects_null_outputs_and_running_timing():
+    L = _lib()
+    n, r = ctypes.c_longlong(-1), ctypes.c_longlong(-1)
+    assert L.attn_timing_reruns(None, ctypes.byref(r)) == attn.ATTN_ERR_INVALID
+    assert L.attn_timing_reruns(ctypes.byref(n), None) == attn.ATTN_ERR_INVALID
+    assert L.attn_timing_begin() == attn.ATTN_OK
+    assert L.attn_timing_reruns(ctypes.byref(n), ctypes.byref(r)) == attn.ATTN_ERR_INVALID
+    assert n.value == 0 and r.value == 0  # cleared on every call
+    ms, k = ctypes.c_double(0.0), ctypes.c_int(0)
+    assert L.attn_timing_end(ctypes.byref(ms), ctypes.byref(k)) == attn.ATTN_OK
 
 
 def _kvw(kn=A, vn=A, ks=A, vs=A, pos=A, col=A, srows=None, T=4, Hkv=2, D=64, rows=32, cols=3,

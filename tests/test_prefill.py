@@ -206,12 +206,25 @@ def _shifted_keys(k, q, scale, logit_of_key):
     return qpos, (k.float() + shift).to(torch.bfloat16)
 
 
+def _count_redone(fn):
+    """(fn(), (attention workgroups, how many of them redid their key range
+    with the exact running maximum)), from the profiling aid around fn."""
+    attn.timing_begin()
+    try:
+        out = fn()
+        torch.cuda.synchronize()
+    finally:
+        attn.timing_end()
+    return out, attn.timing_reruns()
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_logits_far_from_the_first_tile(D, direction):
     """Logits that rise along the keys by ~150 nats overflow the reference
-    taken from the first tile, so the workgroups redo the range exactly;
-    falling logits stay on the fast pass with tiny P.  Both match the oracle."""
+    taken from the first tile unless it is refreshed (D = 128); at D = 64 and
+    256 the workgroups redo the range exactly.  Falling logits stay on the
+    fast pass with tiny P.  All match the oracle."""
     B, Hq, Hkv, Lq, Lkv = 1, 8, 2, 64, 2000
     say("logits", direction, "D", D)
     q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=25)
@@ -225,10 +238,32 @@ def test_logits_far_from_the_first_tile(D, direction):
     compare(out, ref, "logits %s D %d" % (direction, D))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_rising_logits_refresh_the_reference(D, splits, monkeypatch):
+    """Logits rising by 150 nats over 2000 keys (0.11 in log2 units per key):
+    at D = 128 the periodic refresh of the fixed references keeps every sum
+    in range, so no workgroup redoes its range; at D = 64 and 256, which have
+    no refresh, some do.  Split or not, the output matches the oracle."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
+    B, Hq, Hkv, Lq, Lkv = 1, 8, 2, 64, 2000
+    say("refresh, D", D, "splits", splits)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=28)
+    scale = 1.0 / math.sqrt(D)
+    q, k = _shifted_keys(k, q, scale, torch.linspace(0.0, 150.0, Lkv))
+    out, (wg, redone) = _count_redone(lambda: _run(q, k, v, scale=scale))
+    say("  workgroups", wg, "redone", redone)
+    ref = oracle.prefill(q, k, v, scale)
+    compare(out, ref, "refresh D %d splits %d" % (D, splits))
+    assert wg > 0
+    assert (redone > 0) == (D != 128)
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_rising_logits_with_splits(splits, monkeypatch):
-    """Each split keeps its own reference; splits whose logits outgrow it are
-    redone exactly and the merge combines both kinds of partials."""
+    """Each split keeps its own reference; a split whose logits rise faster
+    than the refresh follows (200 nats over its last 1000 keys) is redone
+    exactly, and the merge combines both kinds of partials."""
     monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
     B, Hq, Hkv, Lq, Lkv, D = 1, 8, 2, 96, 3000, 128
     say("rising logits, splits", splits)
@@ -237,9 +272,11 @@ def test_rising_logits_with_splits(splits, monkeypatch):
     ramp = torch.zeros(Lkv)
     ramp[2000:] = torch.linspace(0.0, 200.0, Lkv - 2000)  # only the last split outgrows
     q, k = _shifted_keys(k, q, scale, ramp)
-    out = _run(q, k, v, scale=scale)
+    out, (wg, redone) = _count_redone(lambda: _run(q, k, v, scale=scale))
+    say("  workgroups", wg, "redone", redone)
     ref = oracle.prefill(q, k, v, scale)
     compare(out, ref, "rising logits, splits %d" % splits)
+    assert 0 < redone < wg if splits > 1 else redone == wg
 
 
 def test_windowed_rows_with_very_negative_logits():
