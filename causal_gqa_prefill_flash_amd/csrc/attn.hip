@@ -1690,6 +1690,39 @@ __device__ bool pick_item(const VarlenArgs& a, int P, int hg, int gq, int L, int
     return sh_seg >= 0;
 }
 
+// The same choice made by each wave on its own when the table has at most
+// 64 segments: lane i plans segment i, and each lane sums the item counts of
+// the segments ordered before its own from the other lanes' plans (readlane),
+// so there is no LDS and no barrier, and one round of table loads.
+__device__ bool pick_item_wave(const VarlenArgs& a, int P, int hg, int gq, int L, int* j_out,
+                               Segment* sg_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool has = lane < a.S;
+    const Segment xs = has ? read_segment(a, lane) : Segment{};
+    const SegPlan ps = has ? seg_plan(xs, P, hg, gq, a.Hkv, a.split_keys, a.nsplit)
+                           : SegPlan{0, 1, 0, 0, false};
+    int64_t off = 0;
+    for (int i = 0; i < a.S; ++i) {
+        const int c2 = __builtin_amdgcn_readlane(ps.cost, i);
+        const int n2 = __builtin_amdgcn_readlane(ps.count, i);
+        if (c2 > ps.cost || (c2 == ps.cost && i < lane)) off += n2;
+    }
+    const bool mine = has && ps.count > 0 && L >= off && L < off + ps.count;
+    const uint64_t m = __ballot(mine);
+    if (!m) return false;
+    const int w = __builtin_ctzll(m);  // the item ranges are disjoint: one lane
+    *j_out = __builtin_amdgcn_readlane((int)(L - off), w);
+    sg_out->q_start = __builtin_amdgcn_readlane(xs.q_start, w);
+    sg_out->q_len = __builtin_amdgcn_readlane(xs.q_len, w);
+    sg_out->col = __builtin_amdgcn_readlane(xs.col, w);
+    sg_out->kv_end = __builtin_amdgcn_readlane(xs.kv_end, w);
+    sg_out->causal = __builtin_amdgcn_readlane(xs.causal, w);
+    sg_out->window = __builtin_amdgcn_readlane(xs.window, w);
+    sg_out->R = __builtin_amdgcn_readlane(xs.R, w);
+    sg_out->flags = 0;
+    return true;
+}
+
 // ---------------------------------------------------------------- decode items
 //
 // Few rows and many keys: such an item is bound by the K/V stream, so every
@@ -1894,7 +1927,9 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     // this workgroup's work item: (segment, item j of that segment)
     int seg, j;
     Segment sg;
-    if (!pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j, &sg)) return;
+    const bool got = a.S <= kWave ? pick_item_wave(a, rm.P, hg, g, blockIdx.x, &j, &sg)
+                                  : pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j, &sg);
+    if (!got) return;
     const SegPlan pl = seg_plan(sg, rm.P, hg, g, a.Hkv, a.split_keys, a.nsplit);
     if (pl.decode) {
         __shared__ __attribute__((aligned(1024))) u16 sx[2 * kBN * D];
