@@ -1457,22 +1457,44 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
 // Merge the split partials (store_partial) of one row: M = max m_s, w_s =
 // 2^(m_s - M); split s adds w_s l_s 2^e_s times its fp16 values to the
 // numerator and w_s l_s to the denominator; o = numerator / denominator (0
-// when it is 0).  The splits are read in groups of G whose loads are all in
-// flight together (indices past nsplit are clamped and weighted 0); groups
-// merge by the same rule.
-template <int D, int G = 8>
+// when it is 0).  This thread merges values [d0, d0 + W), W = 4 or 8.  The
+// splits are read in groups of G whose loads are all in flight together
+// (indices past nsplit are clamped and weighted 0); groups merge by the same
+// rule.
+template <int W>
+struct HalfW;  // W fp16 values as one load
+template <>
+struct HalfW<4> {
+    uint32_t h[2];
+    __device__ static HalfW load(const u16* p) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        return HalfW{{x.x, x.y}};
+    }
+};
+template <>
+struct HalfW<8> {
+    uint32_t h[4];
+    __device__ static HalfW load(const u16* p) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        return HalfW{{x.x, x.y, x.z, x.w}};
+    }
+};
+
+template <int D, int G = 8, int W = 4>
 __device__ inline void combine_row(const u16* po, const float* pml, int64_t split_stride_o,
                                      int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
     float M = -INFINITY, L = 0.f;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) acc[i] = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += G) {
         float4 r[G];
-        uint2 x[G];
+        HalfW<W> x[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const int sj = min(s0 + j, nsplit - 1);
             r[j] = *reinterpret_cast<const float4*>(pml + sj * split_stride_ml);
-            x[j] = *reinterpret_cast<const uint2*>(po + sj * split_stride_o + d0);
+            x[j] = HalfW<W>::load(po + sj * split_stride_o + d0);
         }
         float Mg = M;
 #pragma unroll
@@ -1481,28 +1503,33 @@ __device__ inline void combine_row(const u16* po, const float* pml, int64_t spli
         if (Mg == -INFINITY) continue;  // nothing visible so far
         const float rs = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mg);
         L *= rs;
-        acc[0] *= rs;
-        acc[1] *= rs;
-        acc[2] *= rs;
-        acc[3] *= rs;
+#pragma unroll
+        for (int i = 0; i < W; ++i) acc[i] *= rs;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const float w = (s0 + j < nsplit && r[j].x != -INFINITY)
                                 ? __builtin_amdgcn_exp2f(r[j].x - Mg) : 0.f;
-            const f16x2 lo = __builtin_bit_cast(f16x2, x[j].x), hi = __builtin_bit_cast(f16x2, x[j].y);
             const float wz = w * r[j].z;
             L += w * r[j].y;
-            acc[0] += wz * (float)lo[0];
-            acc[1] += wz * (float)lo[1];
-            acc[2] += wz * (float)hi[0];
-            acc[3] += wz * (float)hi[1];
+#pragma unroll
+            for (int k = 0; k < W / 2; ++k) {
+                const f16x2 p2 = __builtin_bit_cast(f16x2, x[j].h[k]);
+                acc[2 * k] += wz * (float)p2[0];
+                acc[2 * k + 1] += wz * (float)p2[1];
+            }
         }
         M = Mg;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const uint2 o = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                               pack_bf16x2(acc[2] * inv, acc[3] * inv));
-    *reinterpret_cast<uint2*>(orow + d0) = o;
+    if (W == 4) {
+        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                                          pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    } else {
+        *reinterpret_cast<uint4*>(orow + d0) =
+            make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                       pack_bf16x2(acc[4 % W] * inv, acc[5 % W] * inv),
+                       pack_bf16x2(acc[6 % W] * inv, acc[7 % W] * inv));
+    }
 }
 
 template <int D>
@@ -2006,63 +2033,78 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 
 // Finish pass, one packed row per workgroup: merge split partials, zero a
 // row that no valid segment covers, and record this workgroup's error word
-// (workgroup 0 also reports every segment's flags).
+// (workgroup 0 also reports every segment's flags).  With at most 64
+// segments each wave finds the row's segments on its own (lane s checks
+// segment s; the lowest covering one owns the row); else through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
-    __shared__ int flags_sh, owner_sh, count_sh, ns_sh;
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
     const int t = blockIdx.x;
-    if (threadIdx.x == 0) {
-        flags_sh = 0;
-        owner_sh = 0x7fffffff;
-        count_sh = 0;
-    }
-    __syncthreads();
-    int flags = 0, mine = -1, my_ns = 1;
-    for (int s = threadIdx.x; s < a.S; s += 256) {
-        const Segment x = read_segment(a, s);
-        if (blockIdx.x == 0) flags |= x.flags;
-        if (!x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len) {
-            atomicMin(&owner_sh, s);
-            atomicAdd(&count_sh, 1);
-            if (mine < 0) {  // this thread's first (lowest) covering segment
-                mine = s;
-                my_ns = seg_plan(x, rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys, a.nsplit)
-                            .nsplit;
-            }
+    int flags = 0, owner = -1, count = 0, ns = 1;
+    if (a.S <= kWave) {
+        const int lane = threadIdx.x & (kWave - 1);
+        const bool has = lane < a.S;
+        const Segment x = has ? read_segment(a, lane) : Segment{};
+        const bool cov = has && !x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len;
+        const uint64_t m = __ballot(cov);
+        count = __builtin_popcountll(m);
+        if (m) {
+            owner = __builtin_ctzll(m);
+            const int my_ns =
+                cov ? seg_plan(x, rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys, a.nsplit).nsplit
+                    : 1;
+            ns = __builtin_amdgcn_readlane(my_ns, owner);
         }
-    }
-    if (flags) atomicOr(&flags_sh, flags);
-    __syncthreads();
-    // the thread that read the owning segment publishes its split count
-    if (mine >= 0 && mine == owner_sh) ns_sh = my_ns;
-    __syncthreads();
-    if (t < a.T) {
-        const int owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
-        const int ns = owner >= 0 ? ns_sh : 1;
-        if (owner < 0 || ns > 1) {
-            constexpr int TPR = D / 4;  // threads per (row, head), 4 dims each
-            for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
-                const int h = e / TPR, d0 = (e % TPR) * 4;
-                u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
-                if (owner < 0) {
-                    *reinterpret_cast<uint2*>(orow + d0) = make_uint2(0, 0);
-                } else {
-                    const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
-                    // all of a row's loads in flight at once, in the narrower
-                    // group when it holds every split
-                    if (ns > 8)
-                        combine_row<D, kMaxVarlenSplits>(a.part_o + row * D,
-                                                           a.part_ml + row * 4, D, 4, ns, d0, orow);
-                    else
-                        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0,
-                                            orow);
+        if (blockIdx.x == 0)
+            for (int b = 1; b <= ATTN_SEG_SPAN; b <<= 1) flags |= __ballot(x.flags & b) ? b : 0;
+    } else {
+        __shared__ int flags_sh, owner_sh, count_sh, ns_sh;
+        if (threadIdx.x == 0) {
+            flags_sh = 0;
+            owner_sh = 0x7fffffff;
+            count_sh = 0;
+        }
+        __syncthreads();
+        int fl = 0, mine = -1, my_ns = 1;
+        for (int s = threadIdx.x; s < a.S; s += 256) {
+            const Segment x = read_segment(a, s);
+            if (blockIdx.x == 0) fl |= x.flags;
+            if (!x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len) {
+                atomicMin(&owner_sh, s);
+                atomicAdd(&count_sh, 1);
+                if (mine < 0) {  // this thread's first (lowest) covering segment
+                    mine = s;
+                    my_ns = seg_plan(x, rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys, a.nsplit)
+                                .nsplit;
                 }
             }
         }
+        if (fl) atomicOr(&flags_sh, fl);
+        __syncthreads();
+        // the thread that read the owning segment publishes its split count
+        if (mine >= 0 && mine == owner_sh) ns_sh = my_ns;
+        __syncthreads();
+        flags = flags_sh;
+        count = count_sh;
+        owner = owner_sh == 0x7fffffff ? -1 : owner_sh;
+        ns = owner >= 0 ? ns_sh : 1;
     }
-    if (threadIdx.x == 0) a.err[blockIdx.x] = flags_sh | (count_sh > 1 ? ATTN_SEG_OVERLAP : 0);
+    if (t < a.T && (owner < 0 || ns > 1)) {
+        constexpr int TPR = D / 8;  // threads per (row, head), 8 dims each
+        for (int e = threadIdx.x; e < a.Hq * TPR; e += 256) {
+            const int h = e / TPR, d0 = (e % TPR) * 8;
+            u16* orow = a.out + (int64_t)t * a.os[0] + (int64_t)h * a.os[1];
+            if (owner < 0) {
+                *reinterpret_cast<uint4*>(orow + d0) = make_uint4(0, 0, 0, 0);
+            } else {
+                const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
+                // eight splits' loads in flight at a time
+                combine_row<D, 8, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0, orow);
+            }
+        }
+    }
+    if (threadIdx.x == 0) a.err[blockIdx.x] = flags | (count > 1 ? ATTN_SEG_OVERLAP : 0);
 }
 
 // ---------------------------------------------------------------- slot write
