@@ -153,6 +153,40 @@ def test_two_segments_of_one_sequence():
     compare(out, ref, "two segments per sequence")
 
 
+@pytest.mark.parametrize("S", [64, 65, 150])
+def test_tables_past_64_segments(S):
+    """Up to 64 segments each wave of the attention kernel and of the finish
+    pass plans the table on its own (a lane per segment); past that both go
+    through LDS.  Tables of 64, 65 and 150 segments (decode rows, 256-row
+    blocks, split and unsplit keys, rings, an invalid segment, gaps) match
+    the oracle either way."""
+    import random
+    rng = random.Random(7000 + S)
+    rows, Hkv, D, Hq = 1536, 2, 64, 8
+    cols = S // 2 + 2
+    info, attr, t = [], [], 0
+    for s in range(S):
+        t += rng.randint(0, 2)
+        q_len = rng.choice([1, 2, 3, 5, 40])
+        col = s // 2
+        ring = rng.choice([0, 0, 0, 700])
+        kv_end = rng.randint(q_len, rows if not ring else 2 * ring)
+        window = ring - q_len + 1 if ring else rng.choice([0, 0, 100])
+        info.append((t, q_len, col, kv_end))
+        attr.append((1, window, ring))
+        t += q_len
+    info[S // 3] = (info[S // 3][0], info[S // 3][1], cols - 1, 5)  # the scratch column: invalid
+    T = t + 3
+    say("varlen table of", S, "segments, T", T)
+    info = torch.tensor(info, dtype=torch.int32)
+    attr = torch.tensor(attr, dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=70 + S)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == attn.SEG_COL
+    compare(out, ref, "%d segments" % S)
+
+
 def test_single_segment_equals_prefill_on_the_column_view():
     say("varlen vs prefill on a strided column")
     rows, cols, Hkv, D, Hq = 4096, 5, 2, 128, 16
