@@ -1567,7 +1567,9 @@ struct VarlenArgs {
     float* part_ml;  // [T][Hq][nsplit][4] (store_partial records)
     int S, T, Hq, Hkv, rows, cols, causal, window, ring_rows;
     int nsplit;      // most key splits of a q-block
-    int split_keys;  // target keys per split
+    int split_keys;  // target keys per split (the finest, when adaptive)
+    int adaptive;    // choose the split per table (choose_split_wave); at most 64 segments
+    int gx;          // workgroups of the attention launch
     float c;
     int negate;
     int64_t qs[3], ks[4], vs[4], os[3];
@@ -1717,17 +1719,48 @@ __device__ bool pick_item(const VarlenArgs& a, int P, int hg, int gq, int L, int
     return sh_seg >= 0;
 }
 
+// Split size for this table, chosen by each wave on its own (lane i plans
+// segment i): the finest of split_keys, x 1.5, x 1.5^2, ... whose items fit
+// the launch, so that a table with many q-blocks takes longer splits and
+// fewer items (one item per workgroup and no empty workgroups when its
+// items fit one round), while one with few rows keeps fine splits.  At
+// split_keys >= rows no range splits, and the launch (at least one
+// workgroup per q-block slot) holds every item of a table whose segments
+// do not overlap.  The same arithmetic on the same table gives every wave
+// of the attention launch and of the finish pass the same choice.  Returns
+// the split size and, in *plan, this lane's segment plan at that size.
+__device__ inline int choose_split_wave(const VarlenArgs& a, const Segment& xs, bool has, int P,
+                                        int hg, int gq, SegPlan* plan) {
+    int sk = a.split_keys;
+    for (;;) {
+        const SegPlan p = has ? seg_plan(xs, P, hg, gq, a.Hkv, sk, a.nsplit)
+                              : SegPlan{0, 1, 0, 0, false};
+        int n = 0;  // the items of the table: a scalar sum over the segments' lanes
+        for (int i = 0; i < a.S; ++i) n += __builtin_amdgcn_readlane(p.count, i);
+        if (n <= a.gx || sk >= a.rows) {
+            *plan = p;
+            return sk;
+        }
+        sk += sk >> 1;
+    }
+}
+
 // The same choice made by each wave on its own when the table has at most
 // 64 segments: lane i plans segment i, and each lane sums the item counts of
 // the segments ordered before its own from the other lanes' plans (readlane),
 // so there is no LDS and no barrier, and one round of table loads.
 __device__ bool pick_item_wave(const VarlenArgs& a, int P, int hg, int gq, int L, int* j_out,
-                               Segment* sg_out) {
+                               Segment* sg_out, int* sk_out) {
     const int lane = threadIdx.x & (kWave - 1);
     const bool has = lane < a.S;
     const Segment xs = has ? read_segment(a, lane) : Segment{};
-    const SegPlan ps = has ? seg_plan(xs, P, hg, gq, a.Hkv, a.split_keys, a.nsplit)
-                           : SegPlan{0, 1, 0, 0, false};
+    SegPlan ps;
+    int sk = a.split_keys;
+    if (a.adaptive)
+        sk = choose_split_wave(a, xs, has, P, hg, gq, &ps);
+    else
+        ps = has ? seg_plan(xs, P, hg, gq, a.Hkv, sk, a.nsplit) : SegPlan{0, 1, 0, 0, false};
+    *sk_out = sk;
     int64_t off = 0;
     for (int i = 0; i < a.S; ++i) {
         const int c2 = __builtin_amdgcn_readlane(ps.cost, i);
@@ -1952,12 +1985,12 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     const int hg = a.Hkv * rm.hchunks;
 
     // this workgroup's work item: (segment, item j of that segment)
-    int seg, j;
+    int seg, j, sk = a.split_keys;
     Segment sg;
-    const bool got = a.S <= kWave ? pick_item_wave(a, rm.P, hg, g, blockIdx.x, &j, &sg)
+    const bool got = a.S <= kWave ? pick_item_wave(a, rm.P, hg, g, blockIdx.x, &j, &sg, &sk)
                                   : pick_item(a, rm.P, hg, g, blockIdx.x, &seg, &j, &sg);
     if (!got) return;
-    const SegPlan pl = seg_plan(sg, rm.P, hg, g, a.Hkv, a.split_keys, a.nsplit);
+    const SegPlan pl = seg_plan(sg, rm.P, hg, g, a.Hkv, sk, a.nsplit);
     if (pl.decode) {
         __shared__ __attribute__((aligned(1024))) u16 sx[2 * kBN * D];
         WaveBufs wb;
@@ -2047,13 +2080,18 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
         const bool has = lane < a.S;
         const Segment x = has ? read_segment(a, lane) : Segment{};
         const bool cov = has && !x.flags && t < a.T && t >= x.q_start && t < x.q_start + x.q_len;
+        const int hg = a.Hkv * rm.hchunks;
+        SegPlan px;
+        if (a.adaptive)
+            (void)choose_split_wave(a, x, has, rm.P, hg, g, &px);
+        else
+            px = has ? seg_plan(x, rm.P, hg, g, a.Hkv, a.split_keys, a.nsplit)
+                     : SegPlan{0, 1, 0, 0, false};
         const uint64_t m = __ballot(cov);
         count = __builtin_popcountll(m);
         if (m) {
             owner = __builtin_ctzll(m);
-            const int my_ns =
-                cov ? seg_plan(x, rm.P, a.Hkv * rm.hchunks, g, a.Hkv, a.split_keys, a.nsplit).nsplit
-                    : 1;
+            const int my_ns = cov ? px.nsplit : 1;
             ns = __builtin_amdgcn_readlane(my_ns, owner);
         }
         if (blockIdx.x == 0)
@@ -2698,12 +2736,19 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
         a.vs[i] = v_str[i];
     }
     hipStream_t s = (hipStream_t)stream;
-    // a bound on the work items of any table: the q-blocks of segments that
-    // share no packed row number at most T / P + S, each with Hkv x hchunks
-    // (kv head, head chunk) pairs and at most nsplit key splits
-    const int64_t gx =
-        ((int64_t)(T + rm.P - 1) / rm.P + S) * ((int64_t)Hkv * rm.hchunks) * nsplit;
+    // q-block slots of any table: the q-blocks of segments that share no
+    // packed row number at most T / P + S, each with Hkv x hchunks (kv head,
+    // head chunk) pairs.  With at most 64 segments (and no split override)
+    // the split size is chosen per table on the device so that its items fit
+    // a launch of one workgroup per compute unit, or per slot when there are
+    // more slots (choose_split_wave); otherwise the launch bounds the items
+    // at the finest split, nsplit per slot.
+    const int64_t slots = ((int64_t)(T + rm.P - 1) / rm.P + S) * ((int64_t)Hkv * rm.hchunks);
+    a.adaptive = S <= kWave && !getenv("ATTN_FORCE_SPLITS") && !getenv("ATTN_VARLEN_SPLIT_KEYS") &&
+                 rows < (1 << 30);
+    const int64_t gx = a.adaptive ? std::max<int64_t>(slots, di.cus) : slots * nsplit;
     if (gx > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
+    a.gx = (int)gx;
     if (gx > 0 && T > 0 && S > 0) {
         dim3 grid((unsigned)gx);
         a.clk = timing_clock();

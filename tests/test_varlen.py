@@ -187,6 +187,24 @@ def test_tables_past_64_segments(S):
     compare(out, ref, "%d segments" % S)
 
 
+@pytest.mark.parametrize("q_len,kv_end", [(2048, 8192), (4096, 8192), (300, 6000)])
+def test_long_segments_take_longer_splits(q_len, kv_end):
+    """The split size is chosen per table on the device: a segment with many
+    q-blocks takes longer key splits so that its items fit the launch (2048
+    rows of 8192 keys at g = 2: 1728-key splits; 4096 rows: 3888-key ones, on
+    a launch of 256 workgroups), and a decode segment beside it takes the
+    same; a short segment keeps 512-key splits.  All match the oracle."""
+    rows, cols, Hkv, D, Hq = 8192, 3, 2, 64, 4
+    say("varlen long segment", q_len, kv_end)
+    info = torch.tensor([(0, q_len, 0, kv_end), (q_len + 2, 1, 1, 8000)], dtype=torch.int32)
+    T = q_len + 3
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=80)
+    out, err = _gpu_varlen(q, ks, vs, info)
+    assert err == 0
+    ref = oracle.varlen(q, ks, vs, info)
+    compare(out, ref, "long segment %d x %d" % (q_len, kv_end))
+
+
 def test_single_segment_equals_prefill_on_the_column_view():
     say("varlen vs prefill on a strided column")
     rows, cols, Hkv, D, Hq = 4096, 5, 2, 128, 16
