@@ -33,6 +33,8 @@ def prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=0):
 PREFILL_WORKLOADS = {
     "tiny": dict(wid=1, B=1, Hq=4, Hkv=1, D=64, Lq=256, Lkv=256, q_pos0=None),
     "d64_lq512_lkv16k": dict(wid=2, B=1, Hq=16, Hkv=2, D=64, Lq=512, Lkv=16384, q_pos0=None),
+    # the same short chunk at D = 128 (a row of the pages' operator table)
+    "d128_lq512_lkv16k": dict(wid=7, B=1, Hq=16, Hkv=2, D=128, Lq=512, Lkv=16384, q_pos0=None),
     "d128_lq1k_lkv128k": dict(wid=3, B=1, Hq=16, Hkv=2, D=128, Lq=1024, Lkv=131072, q_pos0=None),
     # the same, with key positions shifted past the first 16 query positions
     "d128_lq1k_lkv128k_masked16": dict(wid=3, B=1, Hq=16, Hkv=2, D=128, Lq=1024, Lkv=131072,
