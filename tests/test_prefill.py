@@ -161,7 +161,7 @@ def test_deterministic_and_masked_keys_do_not_matter():
 
 # ------------------------------------------------------------- full-size workloads
 
-FULL = ["d64_lq512_lkv16k", "d128_lq1k_lkv128k", "d128_lq1k_lkv128k_masked16",
+FULL = ["d64_lq512_lkv16k", "d128_lq512_lkv16k", "d128_lq1k_lkv128k", "d128_lq1k_lkv128k_masked16",
         "d64_lq4k_lkv128k", "d128_lq4k_lkv128k", "d256_lq512_lkv16k", "d256_lq1k_lkv128k"]
 
 
