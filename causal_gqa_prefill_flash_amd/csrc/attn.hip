@@ -2068,8 +2068,10 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 // row that no valid segment covers, and record this workgroup's error word
 // (workgroup 0 also reports every segment's flags).  With at most 64
 // segments each wave finds the row's segments on its own (lane s checks
-// segment s; the lowest covering one owns the row); else through LDS.
-template <int D>
+// segment s; the lowest covering one owns the row); else through LDS.  G:
+// splits whose loads are in flight together (16 for few packed rows, where
+// the extra registers cost no residency; 8 otherwise).
+template <int D, int G>
 __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     const int g = a.Hq / a.Hkv;
     const RowMap rm = row_map(g);
@@ -2137,8 +2139,7 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
                 *reinterpret_cast<uint4*>(orow + d0) = make_uint4(0, 0, 0, 0);
             } else {
                 const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
-                // eight splits' loads in flight at a time
-                combine_row<D, 8, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0, orow);
+                combine_row<D, G, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0, orow);
             }
         }
     }
@@ -2761,10 +2762,15 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen launch failed");
     }
     dim3 fgrid((unsigned)varlen_finish_blocks(T));
+    // few packed rows: one finish workgroup per row fits the CUs at any
+    // residency, so all 16 splits' loads can be in flight at once
+    const bool few = T <= 2 * di.cus;
     if (D == 64)
-        hipLaunchKernelGGL(varlen_finish_kernel<64>, fgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((few ? varlen_finish_kernel<64, 16> : varlen_finish_kernel<64, 8>),
+                           fgrid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(varlen_finish_kernel<128>, fgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((few ? varlen_finish_kernel<128, 16> : varlen_finish_kernel<128, 8>),
+                           fgrid, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen finish launch failed");
     return ATTN_OK;
 }
