@@ -2739,14 +2739,15 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     hipStream_t s = (hipStream_t)stream;
     // q-block slots of any table: the q-blocks of segments that share no
     // packed row number at most T / P + S, each with Hkv x hchunks (kv head,
-    // head chunk) pairs.  With at most 64 segments (and no split override)
-    // the split size is chosen per table on the device so that its items fit
-    // a launch of one workgroup per compute unit, or per slot when there are
-    // more slots (choose_split_wave); otherwise the launch bounds the items
-    // at the finest split, nsplit per slot.
+    // head chunk) pairs.  When the finest split could need more than two
+    // rounds of workgroups, and the table has at most 64 segments (and no
+    // split override), the split size is chosen per table on the device so
+    // that its items fit a launch of one workgroup per compute unit, or per
+    // slot when there are more slots (choose_split_wave); otherwise the
+    // launch bounds the items at the finest split, nsplit per slot.
     const int64_t slots = ((int64_t)(T + rm.P - 1) / rm.P + S) * ((int64_t)Hkv * rm.hchunks);
     a.adaptive = S <= kWave && !getenv("ATTN_FORCE_SPLITS") && !getenv("ATTN_VARLEN_SPLIT_KEYS") &&
-                 rows < (1 << 30);
+                 rows < (1 << 30) && slots * nsplit > 2 * (int64_t)di.cus;
     const int64_t gx = a.adaptive ? std::max<int64_t>(slots, di.cus) : slots * nsplit;
     if (gx > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "launch grid too large");
     a.gx = (int)gx;
