@@ -259,6 +259,30 @@ def test_rising_logits_refresh_the_reference(D, splits, monkeypatch):
     assert (redone > 0) == (D != 128)
 
 
+@pytest.mark.parametrize("Hq", [8, 4])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_rising_logits_in_a_window(Hq, splits, monkeypatch):
+    """Logits rising 0.12 nats per key (84 nats over a 700-key window: sums
+    far past 2^64 with a fixed reference) under a sliding window.  At g = 4
+    every row of a q-block (64 positions) sees keys of its range's first
+    tile, and the refresh keeps every sum in range: no workgroup reruns.  At
+    g = 2 a q-block spans 128 positions, so some rows see nothing in that
+    tile and keep the reference 0; their first visible logits (about 360 in
+    log2 units) overflow P, and their workgroups redo the range with the
+    exact running maximum.  Both match the oracle."""
+    monkeypatch.setenv("ATTN_FORCE_SPLITS", str(splits))
+    B, Hkv, Lq, Lkv, D, window = 1, 2, 192, 3000, 128, 700
+    say("rising logits in a window, Hq", Hq, "splits", splits)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=29)
+    scale = 1.0 / math.sqrt(D)
+    q, k = _shifted_keys(k, q, scale, torch.linspace(0.0, 0.12 * Lkv, Lkv))
+    out, (wg, redone) = _count_redone(lambda: _run(q, k, v, scale=scale, window=window))
+    say("  workgroups", wg, "redone", redone)
+    ref = oracle.prefill(q, k, v, scale, window=window)
+    compare(out, ref, "rising logits, window %d, Hq %d, splits %d" % (window, Hq, splits))
+    assert wg > 0 and (redone > 0) == (Hq == 4)
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_rising_logits_with_splits(splits, monkeypatch):
     """Each split keeps its own reference; a split whose logits rise faster
