@@ -77,3 +77,41 @@ def test_random_varlen_table(seed):
     say("  flags", flags)
     assert err == flags and flags & ~attn.SEG_SPAN == 0
     compare(out, ref, "random varlen %d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_varlen_tables_with_long_segments(seed):
+    """Seeded tables over an 8192-row store with q_len up to 640 and kv_end up
+    to the store: enough q-block slots that the launch chooses the key-split
+    size per table on the device (coarser splits than 512 keys for the larger
+    tables), with causal, non-causal, windowed and ring segments."""
+    rng = random.Random(9300 + seed)
+    D = rng.choice([64, 128])
+    Hkv = 2
+    Hq = Hkv * rng.choice([2, 4, 8])
+    rows, cols = 8192, 6
+    S = rng.randint(3, 8)
+    info, attr, t = [], [], 0
+    for s_ in range(S):
+        t += rng.randint(0, 3)
+        q_len = rng.choice([1, 3, 40, 200, 640])
+        col = s_ % (cols - 1)
+        causal = rng.choice([1, 1, 0])
+        ring = rng.choice([0, 0, 2559]) if causal else 0
+        R = ring if ring else rows
+        kv_end = rng.randint(q_len, 3 * R if ring else rows)
+        window = (rng.choice([0, 2048]) if not ring else R - q_len + 1) if causal else 0
+        info.append((t, q_len, col, kv_end))
+        attr.append((causal, window, ring))
+        t += q_len
+    T = t + rng.randint(0, 5)
+    say("random long varlen", seed, dict(D=D, Hq=Hq, S=S, T=T))
+    info = torch.tensor(info, dtype=torch.int32)
+    attr = torch.tensor(attr, dtype=torch.int32)
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=400 + seed)
+    out, ws = attn.sdpa_varlen(q.to(dev()), ks.to(dev()), vs.to(dev()), info.to(dev()),
+                               seg_attr=attr.to(dev()))
+    err = attn.varlen_read_error(ws, S, T)
+    ref, flags = oracle.varlen(q, ks, vs, info, seg_attr=attr, return_flags=True)
+    assert err == flags == 0
+    compare(out, ref, "random long varlen %d" % seed)
