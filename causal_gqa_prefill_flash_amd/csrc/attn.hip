@@ -73,7 +73,7 @@ constexpr int kBM = kWaves * 32 * kNT;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxSplits = 16;    // key splits of a prefill launch
 constexpr int kMaxVarlenSplits = 16;  // key splits of one varlen q-block
-constexpr int kVarlenSplitKeys = 512; // varlen: target keys per split of a q-block
+constexpr int kVarlenSplitKeys = 512; // varlen: finest target keys per split of a q-block
 constexpr int kMaxLongSplits = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -742,8 +742,10 @@ __device__ inline void m_phase(const u16* Ks, const u16* Vs, const bf16x8 (*qf)[
 // underflowed are negligible next to a final sum of at least 2^-64.  A wave
 // with no lane share above 2^16 pays a compare.
 constexpr float kRefreshHi = 0x1p16f;
+// D = 64: more VALU work beside the partner wave's MFMA phase lengthens that
+// phase, which bounds the step there; D = 256 runs its own loop
 template <int D>
-constexpr bool kRefresh = D == 128;  // D = 64: the softmax phase is the bound
+constexpr bool kRefresh = D == 128;
 
 template <int D>
 __device__ inline void refresh_reference(TileScores& s, RowState<D>& st) {
