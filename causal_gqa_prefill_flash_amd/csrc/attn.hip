@@ -830,6 +830,14 @@ __device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L,
 // softmax phase also prepares the next step's copy descriptors (K(k+3) into
 // Kn, V(k+2) into Vn): scalar work that would otherwise delay the first
 // MFMA of the next phase.
+//
+// The SIMD's issue arbiter prefers the older of two ready waves, so the MFMA
+// phase of group 1 (the younger waves) loses issue slots to group 0's
+// softmax.  Where it measured faster, the MFMA phase runs at wave priority
+// 2: column-store (varlen) loops, and D = 64, whose copy descriptors are
+// then built after the barrier, which gives the partner's softmax a start
+// before the prioritised MFMAs.  The D = 128 prefill loop measured slower
+// with either change.
 template <int D, bool EXACT, bool PRE, class KV, bool REF = false>
 __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
                                float c, const LaneBounds* lb, TileScores& S, TileP& pk,
@@ -837,12 +845,28 @@ __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf
                                typename TileCopySel<D, KV>::T& ck,
                                typename TileCopySel<D, KV>::T& cv, u16* Kn, u16* Vn) {
     typedef typename TileCopySel<D, KV>::T TC;
+    constexpr bool ring = std::is_same<KV, KVRing>::value;
+    constexpr bool prio = ring || D == 64, late = !ring && D == 64;
+    if (prio) {
+        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     m_phase<D, true, true, PRE>(Kr, Vr, qf, S, pk, st, ck, cv);
+    if (prio) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    }
     copy_wait_barrier<2 * TC::N>();
     v_phase<D, EXACT, PRE, KV, REF>(L, k, c, lb, S, pk, st);
-    ck = k_copy<D>(L, k + 3, Kn);
-    cv = v_copy<D>(L, k + 2, Vn);
+    if (!late) {
+        ck = k_copy<D>(L, k + 3, Kn);
+        cv = v_copy<D>(L, k + 2, Vn);
+    }
     phase_barrier();
+    if (late) {
+        ck = k_copy<D>(L, k + 3, Kn);
+        cv = v_copy<D>(L, k + 2, Vn);
+    }
 }
 
 // Attend the keys [k_lo, k_hi) for the rows of this wave.
