@@ -1483,44 +1483,26 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
 // Merge the split partials (store_partial) of one row: M = max m_s, w_s =
 // 2^(m_s - M); split s adds w_s l_s 2^e_s times its fp16 values to the
 // numerator and w_s l_s to the denominator; o = numerator / denominator (0
-// when it is 0).  This thread merges values [d0, d0 + W), W = 4 or 8.  The
-// splits are read in groups of G whose loads are all in flight together
-// (indices past nsplit are clamped and weighted 0); groups merge by the same
-// rule.
-template <int W>
-struct HalfW;  // W fp16 values as one load
-template <>
-struct HalfW<4> {
-    uint32_t h[2];
-    __device__ static HalfW load(const u16* p) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
-        return HalfW{{x.x, x.y}};
-    }
-};
-template <>
-struct HalfW<8> {
-    uint32_t h[4];
-    __device__ static HalfW load(const u16* p) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        return HalfW{{x.x, x.y, x.z, x.w}};
-    }
-};
-
-template <int D, int G = 8, int W = 4>
+// when it is 0).  This thread merges the 8 values [d0, d0 + 8), one 16-byte
+// load per split.  The splits are read in groups of G whose loads are all in
+// flight together (indices past nsplit are clamped and weighted 0); groups
+// merge by the same rule.
+template <int D, int G>
 __device__ inline void combine_row(const u16* po, const float* pml, int64_t split_stride_o,
                                      int64_t split_stride_ml, int nsplit, int d0, u16* orow) {
+    constexpr int W = 8;
     float M = -INFINITY, L = 0.f;
     float acc[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) acc[i] = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += G) {
         float4 r[G];
-        HalfW<W> x[G];
+        uint4 x[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const int sj = min(s0 + j, nsplit - 1);
             r[j] = *reinterpret_cast<const float4*>(pml + sj * split_stride_ml);
-            x[j] = HalfW<W>::load(po + sj * split_stride_o + d0);
+            x[j] = *reinterpret_cast<const uint4*>(po + sj * split_stride_o + d0);
         }
         float Mg = M;
 #pragma unroll
@@ -1537,9 +1519,10 @@ __device__ inline void combine_row(const u16* po, const float* pml, int64_t spli
                                 ? __builtin_amdgcn_exp2f(r[j].x - Mg) : 0.f;
             const float wz = w * r[j].z;
             L += w * r[j].y;
+            const uint32_t h[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
 #pragma unroll
             for (int k = 0; k < W / 2; ++k) {
-                const f16x2 p2 = __builtin_bit_cast(f16x2, x[j].h[k]);
+                const f16x2 p2 = __builtin_bit_cast(f16x2, h[k]);
                 acc[2 * k] += wz * (float)p2[0];
                 acc[2 * k + 1] += wz * (float)p2[1];
             }
@@ -1547,24 +1530,18 @@ __device__ inline void combine_row(const u16* po, const float* pml, int64_t spli
         M = Mg;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    if (W == 4) {
-        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                                                          pack_bf16x2(acc[2] * inv, acc[3] * inv));
-    } else {
-        *reinterpret_cast<uint4*>(orow + d0) =
-            make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                       pack_bf16x2(acc[4 % W] * inv, acc[5 % W] * inv),
-                       pack_bf16x2(acc[6 % W] * inv, acc[7 % W] * inv));
-    }
+    *reinterpret_cast<uint4*>(orow + d0) =
+        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
-    constexpr int TPR = D / 4;  // threads per row, 4 dims each
+    constexpr int TPR = D / 8;  // threads per row, 8 dims each (one 16-byte load per split)
     int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
     int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
     if (row >= rows) return;
-    int d0 = (threadIdx.x % TPR) * 4;
+    int d0 = (threadIdx.x % TPR) * 8;
     int i = (int)(row % a.Lq);
     int h = (int)((row / a.Lq) % a.Hq);
     int b = (int)(row / ((int64_t)a.Lq * a.Hq));
@@ -1572,11 +1549,11 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     // loads of every split in flight at once, in the narrowest group that
     // holds them (no clamped duplicates)
     if (a.nsplit <= 4)
-        combine_row<D, 4>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
-                            d0, orow);
+        combine_row<D, 4>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4,
+                             a.nsplit, d0, orow);
     else
-        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4, a.nsplit,
-                            d0, orow);
+        combine_row<D, 8>(a.part_o + row * D, a.part_ml + row * 4, rows * D, rows * 4,
+                             a.nsplit, d0, orow);
 }
 
 // ---------------------------------------------------------------- varlen
@@ -2165,7 +2142,7 @@ __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
                 *reinterpret_cast<uint4*>(orow + d0) = make_uint4(0, 0, 0, 0);
             } else {
                 const int64_t row = ((int64_t)t * a.Hq + h) * a.nsplit;
-                combine_row<D, G, 8>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0, orow);
+                combine_row<D, G>(a.part_o + row * D, a.part_ml + row * 4, D, 4, ns, d0, orow);
             }
         }
     }
@@ -2604,7 +2581,7 @@ static int prefill_call(const void* q, const void* k, const void* v, void* out, 
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed");
     if (nsplit > 1) {
         int64_t rows = (int64_t)B * Hq * Lq;
-        int per = 256 / (D / 4);
+        int per = 256 / (D / 8);  // rows per combine workgroup
         int64_t nb = (rows + per - 1) / per;
         if (D == 64)
             hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3((unsigned)nb), dim3(256), 0, s, a);
