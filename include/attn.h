@@ -89,10 +89,9 @@ const char *attn_last_error(void);
  *
  * Layout rules (else ATTN_ERR_UNSUPPORTED): D in {64, 128, 256} (256: the
  * head dimension the page left on its portable path, here a kernel of its
- * own); innermost
- * stride 1 on all four tensors; base pointers 16-byte aligned; every other
- * stride a multiple of 8 elements; k/v row strides (k_str[2], v_str[2])
- * below 2^24 elements.
+ * own); innermost stride 1 on all four tensors; base pointers 16-byte
+ * aligned; every other stride a multiple of 8 elements; k/v row strides
+ * (k_str[2], v_str[2]) below 2^24 elements.
  * Sizes (else ATTN_ERR_INVALID): B, Hq, Hkv >= 1; Lq, Lkv >= 0; Hq % Hkv == 0;
  * all element offsets below 2^62; q/out non-null when Lq > 0 and k/v
  * non-null when Lkv > 0.  Lq == 0 enqueues nothing; Lkv == 0 writes zeros.
