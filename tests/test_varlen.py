@@ -51,6 +51,21 @@ def test_seeded_tables_match_oracle(seed):
     compare(out, ref, "seed %d" % seed)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,seed", [(4, 4, 128, 5101), (6, 2, 64, 5102), (32, 1, 128, 5103),
+                                             (40, 8, 64, 5104)])
+def test_gqa_ratios_match_oracle(Hq, Hkv, D, seed):
+    """Seeded tables at other query heads per KV head (g = 1, 3, 32, 5): the
+    q-block holds 256 / g positions of g heads (85 positions at g = 3), and
+    a segment takes the decode items while q_len * g <= 32."""
+    say("varlen GQA ratio", Hq, Hkv, D, seed)
+    info, attr, T = synth.random_varlen_table(seed)
+    q, ks, vs = synth.varlen_inputs(T, 8192, 9, Hkv, D, Hq, wid=seed)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
+    assert err == 0
+    compare(out, ref, "Hq %d Hkv %d D %d seed %d" % (Hq, Hkv, D, seed))
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_short_query_steps_split_keys(D):
     """Every segment a decode-like step over a full column (the split path)."""
