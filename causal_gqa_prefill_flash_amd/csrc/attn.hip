@@ -630,6 +630,15 @@ struct TileSmem {
     int* rerun;  // set when the fixed-reference pass must be redone exactly
 };
 
+// LDS tile (32 rows x D) of wave w for the row stores: half of a K or V
+// stage, which no wave reads once the key range is done.
+template <int D>
+__device__ inline u16* row_tile(const TileSmem<D>& sm, int w) {
+    const int i = w >> 1;
+    u16* const st = i == 0 ? sm.k[0] : i == 1 ? sm.v[0] : i == 2 ? sm.k[1] : sm.v[1];
+    return st + (w & 1) * 32 * D;
+}
+
 // Per-range constants of the key loop.
 template <int D, class KV>
 struct KeyLoop {
@@ -1006,22 +1015,62 @@ __device__ inline void load_q(bf16x8* qf, const u16* qrow, bool valid, float cq)
     }
 }
 
-// Final normalisation and bf16 store of one row: o / l, 0 when l == 0.
-template <int D>
-__device__ inline void store_out(const f32x16* o, float lpart, u16* orow, bool valid) {
-    const int hh = (threadIdx.x & (kWave - 1)) >> 5;
-    const float l = sum_across_halves(lpart);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (!valid) return;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Row stores through LDS.  The output accumulator leaves lane l of a wave
+// with row l % 32 and the two half-waves with alternate groups of 4 values,
+// so a direct store would write 16 bytes of each of 32 rows per
+// instruction.  Instead the wave writes its rows, packed to 16 bits, into a
+// private LDS tile (32 rows x D; the 16-byte chunk c of row r sits at chunk
+// c ^ (r mod D/8), so that neither the writes nor the reads conflict on the
+// banks), reads them back with D/8 consecutive lanes per row, and stores
+// whole rows in 16-byte pieces.  rowp: this lane's row address, null when
+// the row is not written (the same in both half-waves).  The tile must not
+// be read or written by another wave meanwhile.
+template <int D, bool F16>
+__device__ inline void store_rows(const f32x16* o, float sc, u16* rowp, u16* tile) {
+    constexpr int NC = D / 8, RPI = kWave / NC;  // chunks per row, rows per read
+    const int lane = threadIdx.x & (kWave - 1), r = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const int d = 32 * dt + 8 * a + 4 * hh;
-            const uint2 w = make_uint2(pack_bf16x2(o[dt][4 * a] * inv, o[dt][4 * a + 1] * inv),
-                                       pack_bf16x2(o[dt][4 * a + 2] * inv, o[dt][4 * a + 3] * inv));
-            *reinterpret_cast<uint2*>(orow + d) = w;
+            const int cc = 4 * dt + a;  // values 32dt + 8a + 4hh .. +3: chunk cc, half hh
+            const float x0 = o[dt][4 * a] * sc, x1 = o[dt][4 * a + 1] * sc;
+            const float x2 = o[dt][4 * a + 2] * sc, x3 = o[dt][4 * a + 3] * sc;
+            const uint2 w = F16 ? make_uint2(pack_f16x2(x0, x1), pack_f16x2(x2, x3))
+                                : make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+            *reinterpret_cast<uint2*>(tile + r * D + 8 * (cc ^ (r & (NC - 1))) + 4 * hh) = w;
         }
+    // the reads below see the other lanes' writes (LDS keeps a wave's order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t rp = (uint64_t)rowp;
+    const int c = lane % NC;
+#pragma unroll
+    for (int j = 0; j < 32 / RPI; ++j) {
+        const int R = j * RPI + lane / NC;
+        const uint4 x = *reinterpret_cast<const uint4*>(tile + R * D + 8 * (c ^ (R & (NC - 1))));
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(R << 2, (int)(uint32_t)rp);
+        const uint32_t hi =
+            (uint32_t)__builtin_amdgcn_ds_bpermute(R << 2, (int)(uint32_t)(rp >> 32));
+        u16* q = reinterpret_cast<u16*>(((uint64_t)hi << 32) | lo);
+        if (q) *reinterpret_cast<uint4*>(q + 8 * c) = x;
+    }
+}
+
+// Final normalisation and bf16 store of one row: o / l, 0 when l == 0.
+template <int D>
+__device__ inline void store_out(const f32x16* o, float lpart, u16* orow, bool valid, u16* tile) {
+    const float l = sum_across_halves(lpart);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    store_rows<D, false>(o, inv, valid ? orow : nullptr, tile);
 }
 
 // Split partial of one row (prefill and varlen), at half the bytes of fp32:
@@ -1031,16 +1080,10 @@ __device__ inline void store_out(const f32x16* o, float lpart, u16* orow, bool v
 // rounding moves an element by at most 2^-12 of 2^e, i.e. 2^-11 of the row's
 // largest value.  The record pml holds (m c or -inf when nothing was
 // visible, l, l 2^e, 0) in fp32: the merge weighs the fp16 values by l 2^e.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ inline uint32_t pack_f16x2(float a, float b) {
-    f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-}
 
 template <int D>
 __device__ inline void store_partial(const f32x16* o, float m, float lpart, float c, u16* po,
-                                       float* pml, bool valid) {
+                                       float* pml, bool valid, u16* tile) {
     const int hh = (threadIdx.x & (kWave - 1)) >> 5;
     const float l = sum_across_halves(lpart);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1054,16 +1097,8 @@ __device__ inline void store_partial(const f32x16* o, float m, float lpart, floa
     (void)frexpf(mx, &e);  // mx < 2^e (e = 0 for mx = 0)
     e = e < -100 ? -100 : (e > 127 ? 127 : e);
     const float sc = ldexpf(inv, -e);
+    store_rows<D, true>(o, sc, valid ? po : nullptr, tile);
     if (!valid) return;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int d = 32 * dt + 8 * a + 4 * hh;
-            *reinterpret_cast<uint2*>(po + d) =
-                make_uint2(pack_f16x2(o[dt][4 * a] * sc, o[dt][4 * a + 1] * sc),
-                           pack_f16x2(o[dt][4 * a + 2] * sc, o[dt][4 * a + 3] * sc));
-        }
     if (hh == 0)
         *reinterpret_cast<float4*>(pml) =
             make_float4(l > 0.f ? (m == -INFINITY ? 0.f : m * c) : -INFINITY, l, ldexpf(l, e), 0.f);
@@ -1277,18 +1312,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const float c = PS ? 1.f : a.c;
     const bool redone = attend<D, PS>(kv, k_lo, k_hi, 1, a.window, p_lane, p_min, p_max, qf, c, st, sm);
 
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        if (a.nsplit == 1) {
-            store_out<D>(st.o[nt], st.l[nt],
-                         a.out + b * a.os[0] + (int64_t)hrow[nt] * a.os[1] +
-                             (int64_t)irow[nt] * a.os[2],
-                         valid[nt]);
-        } else {
-            const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[nt]) * a.Lq + irow[nt];
-            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], c, a.part_o + row * D,
-                               a.part_ml + row * 4, valid[nt]);
-        }
+    static_assert(kNT == 1, "one row tile per wave");
+    u16* const tile = row_tile<D>(sm, __builtin_amdgcn_readfirstlane(wave));
+    __syncthreads();  // every wave is done with the stages
+    if (a.nsplit == 1) {
+        store_out<D>(st.o[0], st.l[0],
+                     a.out + b * a.os[0] + (int64_t)hrow[0] * a.os[1] + (int64_t)irow[0] * a.os[2],
+                     valid[0], tile);
+    } else {
+        const int64_t row = (((int64_t)split * a.B + b) * a.Hq + hrow[0]) * a.Lq + irow[0];
+        store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
+                         valid[0], tile);
     }
     clock_add(a.clk, cm, redone);
 }
@@ -1467,15 +1501,19 @@ __global__ __launch_bounds__(kWaves256 * kWave, 1) void prefill256_kernel(Prefil
         }
     }
 
+    // row-store tiles: two waves per stage; every wave is done with them
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    u16* const tile = (wv < 2 ? sk0 : sv0) + (wv & 1) * 32 * D;
+    __syncthreads();
     if (a.nsplit == 1) {
         store_out<D>(st.o[0], st.l[0],
                      a.out + b * a.os[0] + (int64_t)hrow * a.os[1] + (int64_t)irow * a.os[2],
-                     valid);
+                     valid, tile);
     } else {
         const int64_t row =
             (((int64_t)split * a.B + b) * a.Hq + hrow) * a.Lq + irow;
         store_partial<D>(st.o[0], st.m[0], st.l[0], c, a.part_o + row * D, a.part_ml + row * 4,
-                           valid);
+                           valid, tile);
     }
     clock_add(a.clk, cm, redone);
 }
@@ -2052,17 +2090,16 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
     const bool redone =
         attend<D, false>(kv, k_lo, k_hi, sg.causal, sg.window, p_lane, p_min, p_max, qf, a.c, st, sm);
 
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-        const int t = sg.q_start + jrow[nt];
-        if (nsplit == 1) {
-            store_out<D>(st.o[nt], st.l[nt], a.out + (int64_t)t * a.os[0] + (int64_t)hrow[nt] * a.os[1],
-                         valid[nt]);
-        } else {
-            const int64_t row = ((int64_t)t * a.Hq + hrow[nt]) * a.nsplit + split;
-            store_partial<D>(st.o[nt], st.m[nt], st.l[nt], a.c, a.part_o + row * D,
-                               a.part_ml + row * 4, valid[nt]);
-        }
+    u16* const tile = row_tile<D>(sm, __builtin_amdgcn_readfirstlane(wave));
+    __syncthreads();  // every wave is done with the stages
+    const int t = sg.q_start + jrow[0];
+    if (nsplit == 1) {
+        store_out<D>(st.o[0], st.l[0], a.out + (int64_t)t * a.os[0] + (int64_t)hrow[0] * a.os[1],
+                     valid[0], tile);
+    } else {
+        const int64_t row = ((int64_t)t * a.Hq + hrow[0]) * a.nsplit + split;
+        store_partial<D>(st.o[0], st.m[0], st.l[0], a.c, a.part_o + row * D, a.part_ml + row * 4,
+                         valid[0], tile);
     }
     clock_add(a.clk, cm, redone);
 }
