@@ -2109,8 +2109,10 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(VarlenArgs a) {
 // (workgroup 0 also reports every segment's flags).  With at most 64
 // segments each wave finds the row's segments on its own (lane s checks
 // segment s; the lowest covering one owns the row); else through LDS.  G:
-// splits whose loads are in flight together (16 for few packed rows, where
-// the extra registers cost no residency; 8 otherwise).
+// splits whose loads are in flight together: 16 for few packed rows, where
+// the extra registers cost no residency; otherwise 4, whose 57 registers
+// let 8 waves share a SIMD, so a table of ~2000 rows is resident at once
+// (most rows have at most 4 splits).
 template <int D, int G>
 __global__ __launch_bounds__(256) void varlen_finish_kernel(VarlenArgs a) {
     const int g = a.Hq / a.Hkv;
@@ -2804,13 +2806,14 @@ int attn_sdpa_varlen(const void* q, const void* k_store, const void* v_store, vo
     }
     dim3 fgrid((unsigned)varlen_finish_blocks(T));
     // few packed rows: one finish workgroup per row fits the CUs at any
-    // residency, so all 16 splits' loads can be in flight at once
+    // residency, so all 16 splits' loads can be in flight at once; many rows:
+    // the narrow merge for residency
     const bool few = T <= 2 * di.cus;
     if (D == 64)
-        hipLaunchKernelGGL((few ? varlen_finish_kernel<64, 16> : varlen_finish_kernel<64, 8>),
+        hipLaunchKernelGGL((few ? varlen_finish_kernel<64, 16> : varlen_finish_kernel<64, 4>),
                            fgrid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((few ? varlen_finish_kernel<128, 16> : varlen_finish_kernel<128, 8>),
+        hipLaunchKernelGGL((few ? varlen_finish_kernel<128, 16> : varlen_finish_kernel<128, 4>),
                            fgrid, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "varlen finish launch failed");
     return ATTN_OK;
