@@ -160,12 +160,18 @@ def clock_info():
 
 def with_clock(roof, clk, peak, peak_clock_mhz=2400.0):
     """Adds the measured clock and, for a compute peak (which scales with the
-    clock), the fraction of that peak at the measured clock."""
+    clock), the fraction of that peak at the measured clock: at the mean of
+    the timed workgroups, and at the slowest XCD's clock (the XCDs run at
+    different clocks, equal work per XCD, so the slowest one sets the end)."""
     roof.update(clk)
     if peak and clk.get("sclk_mhz"):
         p = peak * clk["sclk_mhz"] / peak_clock_mhz
         roof["peak_at_sclk"] = round(p, 1)
         roof["frac_at_sclk"] = round(roof["achieved"] / p, 4)
+        ran = [x for x in clk.get("sclk_per_xcd_mhz", []) if x > 0]
+        if ran:
+            pm = peak * min(ran) / peak_clock_mhz
+            roof["frac_at_slowest_xcd_sclk"] = round(roof["achieved"] / pm, 4)
     return roof
 
 
