@@ -481,14 +481,25 @@ __device__ inline void update_max(const TileScores& s, float c, float* m, float*
 }
 
 // P = 2^(s c - m c) rounded to packed bf16 pairs (the B operand of the PV
-// MFMA), and the row sums of P before rounding.  Masked scores are -inf and
-// c > 0, so they give exactly 0.  The sums use plain adds: the packed dot
-// product would wait on the matrix core while the partner wave's MFMAs run.
+// MFMA), and the row sums of P.  Masked scores are -inf and c > 0, so they
+// give exactly 0.  The sums use plain adds: the packed dot product would wait
+// on the matrix core while the partner wave's MFMAs run.
+//
+// Which values the sums add: with a fixed reference the largest weight of a
+// row is not 1, so its bf16 rounding (up to 2^-9 of itself) moves the output
+// by up to 2^-9 of a V value when one key dominates, on top of the output's
+// own rounding.  Adding the rounded weights (RS) makes the normalizer the sum
+// of the weights the PV product used, and that error cancels.  It costs two
+// VALU instructions per pair, 2.4-5.6 % of a prefill call with the scale in
+// Q.  So the fixed-reference pass takes it where the softmax can be sharper
+// than at the standard scale (exact Q: |scale| above 1/sqrt(D); varlen,
+// where it measured free) and keeps the unrounded sums with the scale in Q;
+// the exact pass, which redoes a whole range when needed, always takes it.
 typedef uint32_t TileP[kNT][2][8];
 
 // PRE: s already holds s - m (qk_tile from the negated references), and
-// c = 1, so P = 2^s.
-template <bool PRE = false>
+// c = 1, so P = 2^s.  RS: the sums add the rounded weights.
+template <bool PRE = false, bool RS = true>
 __device__ inline void softmax_tile(const TileScores& s, float c, const float* m, TileP& pk,
                                     float* lsum) {
 #pragma unroll
@@ -502,9 +513,10 @@ __device__ inline void softmax_tile(const TileScores& s, float c, const float* m
                 const float x0 = __builtin_amdgcn_exp2f(PRE ? s[nt][t][r] : fmaf(s[nt][t][r], c, -mc));
                 const float x1 =
                     __builtin_amdgcn_exp2f(PRE ? s[nt][t][r + 1] : fmaf(s[nt][t][r + 1], c, -mc));
-                pk[nt][t][r >> 1] = pack_bf16x2(x0, x1);
-                ls[(r >> 1) & 3] += x0;
-                ls[(r >> 1) & 3] += x1;
+                const uint32_t p2 = pack_bf16x2(x0, x1);  // element 0 in the low half
+                pk[nt][t][r >> 1] = p2;
+                ls[(r >> 1) & 3] += RS ? __uint_as_float(p2 << 16) : x0;
+                ls[(r >> 1) & 3] += RS ? __uint_as_float(p2 & 0xffff0000u) : x1;
             }
         lsum[nt] = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
@@ -791,7 +803,7 @@ __device__ inline void refresh_reference(TileScores& s, RowState<D>& st) {
 // and l when it moves.  Otherwise against the row's fixed reference st.m (0
 // while it is -inf), with no maxima and no rescale; the caller checks
 // afterwards that every row's sum stayed in range.
-template <int D, bool EXACT, bool PRE, class KV, bool REF = false>
+template <int D, bool EXACT, bool PRE, class KV, bool REF = false, bool RS = true>
 __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const LaneBounds* lb,
                                TileScores& S, TileP& pk, RowState<D>& st) {
     if (L.needs_mask(k)) mask_tile(S, L.k0(k), lb);
@@ -802,7 +814,7 @@ __device__ inline void v_phase(const KeyLoop<D, KV>& L, int k, float c, const La
         rescale<D>(alpha, st);
     }
     float lsum[kNT];
-    softmax_tile<PRE>(S, c, st.m, pk, lsum);
+    softmax_tile<PRE, RS>(S, c, st.m, pk, lsum);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) st.l[nt] += lsum[nt];
     pin_v_outputs<D>(pk, st);
@@ -847,7 +859,7 @@ __device__ inline typename TileCopySel<D, KV>::T v_copy(const KeyLoop<D, KV>& L,
 // then built after the barrier, which gives the partner's softmax a start
 // before the prioritised MFMAs.  The D = 128 prefill loop measured slower
 // with either change.
-template <int D, bool EXACT, bool PRE, class KV, bool REF = false>
+template <int D, bool EXACT, bool PRE, class KV, bool REF = false, bool RS = true>
 __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf)[D / 16],
                                float c, const LaneBounds* lb, TileScores& S, TileP& pk,
                                RowState<D>& st, const u16* Kr, const u16* Vr,
@@ -866,7 +878,7 @@ __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf
         __builtin_amdgcn_s_setprio(0);
     }
     copy_wait_barrier<2 * TC::N>();
-    v_phase<D, EXACT, PRE, KV, REF>(L, k, c, lb, S, pk, st);
+    v_phase<D, EXACT, PRE, KV, REF, RS>(L, k, c, lb, S, pk, st);
     if (!late) {
         ck = k_copy<D>(L, k + 3, Kn);
         cv = v_copy<D>(L, k + 2, Vn);
@@ -896,7 +908,7 @@ __device__ inline void pp_step(const KeyLoop<D, KV>& L, int k, const bf16x8 (*qf
 //   p_lane[nt]: position of this lane's row in row tile nt; p_min/p_max:
 //   extreme positions of the workgroup's rows (for the per-tile mask
 //   decision).
-template <int D, bool EXACT, bool PRE, class KV>
+template <int D, bool EXACT, bool PRE, class KV, bool RS>
 __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int window,
                              const int64_t* p_lane, int64_t p_min, int64_t p_max,
                              const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
@@ -943,7 +955,7 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     qk_tile<D>(sm.k[0], qf, S, ck, cv);
     pin_m_outputs<D>(S, st, true, false);
     copy_wait_barrier<2 * TC::N>();
-    v_phase<D, true, false>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
+    v_phase<D, true, false, KV, false, RS>(L, 0, c, lb, S, pk, st);  // tile 0 sets the references
     if (PRE) set_reference<D>(st);
     ck = k_copy<D>(L, 3, sm.k[0]);
     cv = v_copy<D>(L, 2, sm.v[2]);
@@ -952,19 +964,21 @@ __device__ void attend_range(const KV& kv, int k_lo, int k_hi, int causal, int w
     for (; k + 2 < n; k += 3) {
         // k = 1 mod 3: K(k) in stage 1, V(k-1) in stage 0; copies of K(k+2) -> 0,
         // V(k+1) -> 2 (ck, cv); the next step's go to K stage 1, V stage 0
-        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
-        pp_step<D, EXACT, PRE>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
-                          sm.v[1]);
-        pp_step<D, EXACT, PRE, KV, kRefresh<D>>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0], sm.v[2], ck,
-                                              cv, sm.k[0], sm.v[2]);
+        pp_step<D, EXACT, PRE, KV, false, RS>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv,
+                                             sm.k[1], sm.v[0]);
+        pp_step<D, EXACT, PRE, KV, false, RS>(L, k + 1, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck,
+                                             cv, sm.k[2], sm.v[1]);
+        pp_step<D, EXACT, PRE, KV, kRefresh<D>, RS>(L, k + 2, qf, c, lb, S, pk, st, sm.k[0],
+                                                   sm.v[2], ck, cv, sm.k[0], sm.v[2]);
     }
     if (k < n) {
-        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv, sm.k[1], sm.v[0]);
+        pp_step<D, EXACT, PRE, KV, false, RS>(L, k, qf, c, lb, S, pk, st, sm.k[1], sm.v[0], ck, cv,
+                                             sm.k[1], sm.v[0]);
         ++k;
     }
     if (k < n) {
-        pp_step<D, EXACT, PRE>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv, sm.k[2],
-                          sm.v[1]);
+        pp_step<D, EXACT, PRE, KV, false, RS>(L, k, qf, c, lb, S, pk, st, sm.k[2], sm.v[1], ck, cv,
+                                             sm.k[2], sm.v[1]);
         ++k;
     }
     // M(n): PV of tile n-1, whose V sits in stage (n-1) % 3; then no copy
@@ -1144,7 +1158,7 @@ __device__ bool attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
                        const bf16x8 (*qf)[D / 16], float c, RowState<D>& st,
                        const TileSmem<D>& sm) {
     if (threadIdx.x == 0) *sm.rerun = 0;
-    attend_range<D, false, PS>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
+    attend_range<D, false, PS, KV, !PS>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
                                sm);
     bool bad = false;
 #pragma unroll
@@ -1157,7 +1171,7 @@ __device__ bool attend(const KV& kv, int k_lo, int k_hi, int causal, int window,
     __syncthreads();
     if (!*sm.rerun) return false;
     init_state<D>(st);
-    attend_range<D, true, false>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
+    attend_range<D, true, false, KV, true>(kv, k_lo, k_hi, causal, window, p_lane, p_min, p_max, qf, c, st,
                                  sm);
     return true;
 }
@@ -1385,7 +1399,7 @@ __device__ inline void tile256(const u16* kb, const u16* vb, int64_t krs, int64_
         if (PS && FIRST && !EXACT) set_reference<D>(st);
     }
     TileP pk;
-    softmax_tile<PRE>(S, c, st.m, pk, lsum);
+    softmax_tile<PRE, !PS>(S, c, st.m, pk, lsum);
     st.l[0] += lsum[0];
     pv_tile<D>(Vc, pk, st, NoCopy{});
 }

@@ -218,6 +218,26 @@ def _count_redone(fn):
     return out, attn.timing_reruns()
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lkv,D,q_pos0,window,wid", [
+    (2, 16, 4, 59, 1262, 256, 1203, 370, 297),
+    (2, 16, 2, 88, 763, 256, 146, 368, 394),
+    (1, 16, 2, 178, 427, 256, 230, 0, 274),
+    (1, 8, 2, 119, 1326, 128, 76, 0, 401),
+])
+def test_sharp_softmax_rounds_like_its_weights(B, Hq, Hkv, Lq, Lkv, D, q_pos0, window, wid):
+    """Scale 0.2, 2.3-3.2 times the standard scale: logits with a standard
+    deviation near 3, so a row's output is close to one V row.  With a fixed
+    reference the largest weight is not 1 and its bf16 rounding would move
+    such an output by up to 2^-9 of that V value on top of the output's own
+    rounding (max-abs up to 2e-2 on these shapes); the kernels' row sums add
+    the rounded weights there, which cancels it."""
+    say("sharp softmax", B, Hq, Hkv, Lq, Lkv, D, q_pos0, window)
+    q, k, v = synth.prefill_inputs(B, Hq, Hkv, Lq, Lkv, D, wid=wid)
+    out = _run(q, k, v, scale=0.2, q_pos0=q_pos0, window=window)
+    ref = oracle.prefill(q, k, v, 0.2, q_pos0=q_pos0, window=window)
+    compare(out, ref, "sharp softmax D=%d" % D)
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_logits_far_from_the_first_tile(D, direction):
