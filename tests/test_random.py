@@ -16,7 +16,7 @@ from gpu_util import compare, dev, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_prefill_shape(seed):
     rng = random.Random(9100 + seed)
     D = rng.choice([64, 128, 256])
@@ -40,7 +40,7 @@ def test_random_prefill_shape(seed):
     compare(out, ref, "random prefill %d" % seed)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_varlen_table(seed):
     rng = random.Random(9200 + seed)
     D = rng.choice([64, 128])
@@ -79,7 +79,7 @@ def test_random_varlen_table(seed):
     compare(out, ref, "random varlen %d" % seed)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_varlen_tables_with_long_segments(seed):
     """Seeded tables over an 8192-row store with q_len up to 640 and kv_end up
     to the store: enough q-block slots that the launch chooses the key-split
