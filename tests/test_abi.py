@@ -123,6 +123,33 @@ def test_prefill_noalloc_validates_like_prefill(kw, code):
     assert attn.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+def test_error_messages_are_per_thread():
+    """attn_last_error is thread-local: threads that fail validation in
+    different ways, and one whose calls succeed, each read back their own
+    result while the others run (ctypes drops the GIL inside the calls)."""
+    import threading
+    _lib()
+    cases = [(dict(D=96), attn.ATTN_ERR_UNSUPPORTED, "head dim 96"),
+             (dict(B=0), attn.ATTN_ERR_INVALID, "sizes must satisfy"),
+             (dict(Lq=0), attn.ATTN_OK, "")]
+    bad = []
+
+    def run(kw, code, msg):
+        for _ in range(3000):
+            rc = _prefill(**kw)
+            err = attn.last_error()
+            if rc != code or (msg not in err if msg else err != ""):
+                bad.append((kw, rc, err))
+                return
+
+    threads = [threading.Thread(target=run, args=c) for c in cases for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
+
+
 def test_prefill_empty_query_is_a_noop():
     assert _prefill(Lq=0) == attn.ATTN_OK
     assert attn.last_error() == ""
