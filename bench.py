@@ -33,8 +33,10 @@ step_pinned the slot write followed by the varlen attention (us per step).
 
 The roofline object also carries the average shader clock the timed
 attention workgroups ran at (per XCD too) and, for the MFMA peak, the
-fraction of the peak at that clock.  timing_protocol gives per-call median
-and min over 7 outer repetitions and the mean of repetitions 3 to 7.
+fraction of the peak at that clock and at the slowest XCD's clock (every
+XCD gets the same work, so the slowest sets the end).  timing_protocol gives
+per-call median and min over 7 outer repetitions and the mean of
+repetitions 3 to 7.
 """
 import argparse
 import hashlib
