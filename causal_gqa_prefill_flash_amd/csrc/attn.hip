@@ -1877,7 +1877,10 @@ __device__ inline void load_k_regs(bf16x8 (&kr)[2][D / 16], const KVRing& kv, in
 
 // This wave alone copies V rows [k0, k0 + 64) into its LDS tile (the layout
 // of the workgroup copies: instruction i fills rows i*ROWS.., chunk c of row
-// r at position c ^ swz(r)); rows at or past k_hi repeat row k_hi - 1.
+// r at position c ^ swz(r)); rows at or past k_hi repeat row k_hi - 1.  The
+// loads are non-temporal: a decode item reads its rows once (short step
+// -1.5 %, benchmark table unchanged; the same on the compute items' copies
+// cost the table 0.3 %, where q-blocks of one segment share key rows).
 template <int D>
 __device__ inline void copy_v_wave(const KVRing& kv, int k0, int k_hi, u16* dst) {
     constexpr int CH = D / 8, ROWS = 64 / CH, INSTR = kBN / ROWS;
@@ -1889,7 +1892,7 @@ __device__ inline void copy_v_wave(const KVRing& kv, int k0, int k_hi, u16* dst)
         const int row = (int)mod_magic((unsigned)k, (unsigned)kv.R, kv.magic);
         __builtin_amdgcn_global_load_lds(
             (glb_void*)(kv.vb + (int64_t)row * kv.vs + 8 * ((lane % CH) ^ swz<D>(r))),
-            (lds_void*)(dst + i * 512), 16, 0, 0);
+            (lds_void*)(dst + i * 512), 16, 0, 2);
     }
 }
 
