@@ -30,6 +30,9 @@ def _run(q, k, v, **kw):
     (2, 8, 2, 129, 700, 256, 0, 0),       # D = 256: queries from position 0
     (1, 8, 2, 200, 900, 256, None, 150),  # D = 256 with a window
     (1, 32, 1, 40, 500, 64, None, 0),     # g = 32
+    (1, 300, 1, 3, 200, 64, None, 0),     # g = 300: head chunks of 256 and 44 rows
+    (1, 600, 2, 2, 130, 128, None, 0),    # the same over two KV heads
+    (1, 150, 1, 5, 300, 256, None, 0),    # D = 256, g = 150: chunks of 128 and 22
     (1, 8, 2, 257, 900, 128, None, 100),  # sliding window
     (1, 8, 2, 129, 129, 64, 0, 1),        # window of one key: returns V rows
     (1, 8, 2, 100, 400, 128, 37, 0),      # q_pos0 inside the prefix: late keys unseen

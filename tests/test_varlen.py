@@ -66,6 +66,23 @@ def test_gqa_ratios_match_oracle(Hq, Hkv, D, seed):
     compare(out, ref, "Hq %d Hkv %d D %d seed %d" % (Hq, Hkv, D, seed))
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(300, 1, 64), (600, 2, 128)])
+def test_head_chunks_match_oracle(Hq, Hkv, D):
+    """g = 300 query heads per KV head: more than the 256 rows of a q-block,
+    so each q-block holds one position of 256 heads and a second head chunk
+    holds the other 44 (a partly filled row block)."""
+    say("varlen head chunks", Hq, Hkv, D)
+    rows, cols = 2048, 4
+    info = torch.tensor([(0, 5, 0, 700), (6, 1, 1, 1500), (8, 3, 2, 64)], dtype=torch.int32)
+    attr = torch.tensor([(1, 0, 0), (1, 256, 0), (0, 0, 0)], dtype=torch.int32)
+    T = 11
+    q, ks, vs = synth.varlen_inputs(T, rows, cols, Hkv, D, Hq, wid=5106)
+    out, err = _gpu_varlen(q, ks, vs, info, attr)
+    ref = oracle.varlen(q, ks, vs, info, seg_attr=attr)
+    assert err == 0
+    compare(out, ref, "head chunks Hq %d Hkv %d D %d" % (Hq, Hkv, D))
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_short_query_steps_split_keys(D):
     """Every segment a decode-like step over a full column (the split path)."""
